@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the selective scan.
+
+This module only draws random numbers and rounds them to the storage dtype;
+it holds none of the scan's arithmetic, so the HIP path and the CPU oracle can
+both be fed from it without sharing any of the method.
+
+Recipe (every workload):
+  * generator ``numpy.random.Generator(PCG64(seed))``; draws in the order
+    dt, u, delta, z, B, C, D (A is deterministic);
+  * A[k, d, n] = -(n + 1) for every direction k and channel d (S4D-real);
+  * dt[k, d] log-uniform in [1e-3, 1e-1] and delta_bias = log(expm1(dt)),
+    the inverse of softplus, so that softplus(delta_bias) = dt;
+  * u, delta, z, B, C, D standard normal float32; u, delta, z, B, C are then
+    rounded to bfloat16 (round to nearest even) for the bf16 workloads and kept
+    as uint16 bit patterns; A, D and delta_bias stay float32.
+
+Layouts (token-major, C-contiguous; K scan directions):
+  u [B][Ku][L][D] (Ku = 1 for the cross scan, otherwise K; the K axis is
+  dropped when K = 1), delta [B][K][L][D], B and C [B][K][L][N], z [B][L][D],
+  A [K][D][N], D and delta_bias [K][D].
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
+_NDIRS = {DIR_FWD: 1, DIR_BWD: 1, DIR_BIDIR: 2, DIR_CROSS2D: 4}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    dim: int
+    seqlen: int
+    dstate: int
+    dir_mode: int
+    dtype: str  # "f32" or "bf16"
+    gated: bool
+    seed: int
+    height: int = 0
+    width: int = 0
+
+    @property
+    def ndirs(self) -> int:
+        return _NDIRS[self.dir_mode]
+
+    @property
+    def elements(self) -> int:
+        return self.ndirs * self.batch * self.dim * self.seqlen * self.dstate
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the scan is specified on (the Vim one in two sizes).
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 16, 64, 4, DIR_FWD, "f32", True, 1001),
+    "mamba130m_layer": Workload("mamba130m_layer", 8, 1536, 2048, 16, DIR_FWD, "bf16", True, 1002),
+    "long_context": Workload("long_context", 1, 2048, 262144, 16, DIR_FWD, "bf16", True, 1003),
+    "vim_bidir_224": Workload("vim_bidir_224", 128, 768, 197, 16, DIR_BIDIR, "bf16", True, 1041),
+    "vim_bidir_1248": Workload("vim_bidir_1248", 1, 768, 97344, 16, DIR_BIDIR, "bf16", True, 1042),
+    "vmamba_ss2d": Workload("vmamba_ss2d", 32, 192, 4096, 16, DIR_CROSS2D, "bf16", False, 1005,
+                            height=64, width=64),
+}
+DECODE_STEPS = 512  # decode steps that continue the mamba130m_layer scan
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (nearest, ties to even); returns uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in, flat_out = x.reshape(-1), out.reshape(-1)
+    step = 1 << 24
+    for s in range(0, flat_in.size, step):
+        v = flat_in[s:s + step].view(np.uint32)
+        r = (v + (np.uint32(0x7FFF) + ((v >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+        r = r.astype(np.uint16)
+        nan = np.isnan(flat_in[s:s + step])
+        if nan.any():
+            r[nan] = np.uint16(0x7FC0)
+        flat_out[s:s + step] = r
+    return out
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32 exactly."""
+    return (np.ascontiguousarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _normal(rng, shape, dtype):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return bf16_bits(x) if dtype == "bf16" else x
+
+
+def make_inputs(w: Workload, seqlen: int | None = None) -> dict:
+    """Draw one input set for workload ``w`` (optionally with another sequence length)."""
+    L = w.seqlen if seqlen is None else seqlen
+    K, Bsz, Dm, N = w.ndirs, w.batch, w.dim, w.dstate
+    Ku = 1 if w.dir_mode == DIR_CROSS2D else K
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    A = np.ascontiguousarray(np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (K, Dm, N)))
+    dt = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), size=(K, Dm)))
+    delta_bias = np.log(np.expm1(dt)).astype(np.float32)
+    ushape = (Bsz, L, Dm) if Ku == 1 else (Bsz, Ku, L, Dm)
+    dshape = (Bsz, L, Dm) if K == 1 else (Bsz, K, L, Dm)
+    bshape = (Bsz, L, N) if K == 1 else (Bsz, K, L, N)
+    u = _normal(rng, ushape, w.dtype)
+    delta = _normal(rng, dshape, w.dtype)
+    z = _normal(rng, (Bsz, L, Dm), w.dtype)
+    B = _normal(rng, bshape, w.dtype)
+    C = _normal(rng, bshape, w.dtype)
+    D = rng.standard_normal(size=(K, Dm), dtype=np.float32)
+    if K == 1:
+        A, D, delta_bias = A.reshape(Dm, N), D.reshape(Dm), delta_bias.reshape(Dm)
+    return dict(u=u, delta=delta, z=z if w.gated else None, B=B, C=C, A=A, D=D,
+                delta_bias=delta_bias)
