@@ -1,0 +1,233 @@
+"""Benchmark of the gfx950 selective scan: one step = one mamba_scan_fwd over one
+batch of the Mamba-130M-shaped layer workload (batch 8, 1536 channels,
+16 states, 2048 tokens, bf16 inputs, fp32 state, silu gate, last_state
+written), inputs already resident in HBM.
+
+Prints one JSON line.  `value` is scan elements (B·D·L·N) per second over the
+timed steps.  `roofline` describes the scan kernel: it is bound by vector-ALU
+issue (every element needs one v_exp_f32, which issues at half rate, and four
+fp32 VALU operations), so the bound reported is "alu" in elements/s, with the
+HBM view alongside.  `cpu_baseline` times the fp64 CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline] [--decode-steps S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Vector-ALU issue model of MI355X (gfx950): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# = 39.32e12 lane-instructions/s.  Per scan element the method needs Δ·A, Δu·B, the
+# state FMA and the readout FMA (4 VALU) plus exp (v_exp_f32, 2 issue slots at half rate).
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
+SLOTS_PER_ELEMENT = 6.0
+ALU_PEAK_ELEM = VALU_LANE_OPS / SLOTS_PER_ELEMENT
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(w) -> int:
+    """Each input read once, each output written once (bf16 = 2 B; A, D, bias, state = 4 B)."""
+    e = 2 if w.dtype == "bf16" else 4
+    K, Bsz, L, Dm, N = w.ndirs, w.batch, w.seqlen, w.dim, w.dstate
+    Ku = 1 if w.dir_mode == 3 else K
+    by = Bsz * Ku * L * Dm * e          # u
+    by += Bsz * K * L * Dm * e          # delta
+    by += (Bsz * L * Dm * e) if w.gated else 0  # z
+    by += 2 * Bsz * K * L * N * e       # B, C
+    by += Bsz * L * Dm * e              # out
+    by += Bsz * K * Dm * N * 4          # last_state
+    by += K * Dm * N * 4 + 2 * K * Dm * 4  # A, D, delta_bias
+    return by
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("include/mamba_scan.h", "selective_state_space_mamba_amd/csrc/mamba_scan.hip",
+              "selective_state_space_mamba_amd/csrc/scan_kernels.h",
+              "selective_state_space_mamba_amd/csrc/device_math.h"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "scan_fwd_%s_counters.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """Time the fp64 oracle on a bounded sample of the workload's (b, d) rows."""
+    import oracle
+    from selective_state_space_mamba_amd import inputs as I
+    x = I.make_inputs(w)
+    threads = min(16, os.cpu_count() or 1)
+    rng = np.random.Generator(np.random.PCG64(3))
+    # calibrate on a few rows, then size the sample to about `budget_s`
+    rows = np.stack([rng.integers(0, w.batch, 64), rng.integers(0, w.dim, 64)], axis=1)
+    t0 = time.perf_counter()
+    oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                dir_mode=w.dir_mode, height=w.height, width=w.width, rows=rows, nthreads=threads)
+    per_row = (time.perf_counter() - t0) / 64
+    n = int(min(w.batch * w.dim, max(64, budget_s / max(per_row, 1e-9))))
+    rows = np.stack([rng.integers(0, w.batch, n), rng.integers(0, w.dim, n)], axis=1)
+    t0 = time.perf_counter()
+    oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
+                dir_mode=w.dir_mode, height=w.height, width=w.width, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    el = n * w.ndirs * w.seqlen * w.dstate
+    return {"value": el / dt, "unit": "scan elements/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d (b, d) rows of %s, all %d tokens and %d states, fp64, %.1f s"
+                      % (n, w.batch * w.dim, w.name, w.seqlen, w.dstate, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba130m_layer")
+    ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps (defeats the 256 MB MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the scan has no multi-GPU path in this build "
+              "(rows shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import selective_state_space_mamba_amd as ms
+    from selective_state_space_mamba_amd import inputs as I
+
+    ms.load_library()
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+
+    def todev(v):
+        if v is None:
+            return None
+        if v.dtype == np.uint16:
+            return torch.from_numpy(v.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+
+    sets = []
+    for s in range(args.sets):
+        x = I.make_inputs(w.with_(seed=w.seed + 1000 * s))
+        sets.append({k: todev(v) for k, v in x.items()})
+    K = w.ndirs
+    kx = () if K == 1 else (K,)
+    outs = [torch.empty((w.batch, w.seqlen, w.dim), dtype=sets[0]["u"].dtype, device=dev) for _ in sets]
+    states = [torch.empty((w.batch,) + kx + (w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in sets]
+    dims = ms.make_dims(w.batch, w.dim, w.seqlen, w.dstate, ms.DTYPE_BF16 if w.dtype == "bf16" else ms.DTYPE_F32,
+                        height=w.height, width=w.width)
+    ws_bytes = ms.workspace_bytes(dims, w.dir_mode)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        ms.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"],
+                    dir_mode=w.dir_mode, height=w.height, width=w.width, out=outs[i % len(sets)],
+                    last_state=states[i % len(sets)], workspace=ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        # timed region: the whole step sequence, wall clock around synchronisations
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        # per-launch durations with HIP events on the launch stream
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record(stream)
+            step(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        launch_ms = [a.elapsed_time(b) for a, b in evs]
+
+    ms_step = wall * 1e3 / args.steps
+    el = w.elements
+    value = el / (wall / args.steps)
+    avg_launch_s = float(np.mean(launch_ms)) * 1e-3
+    alg_bytes = algorithmic_bytes(w)
+    ach_elem = el / avg_launch_s / 1e9
+    hbm_gbs = alg_bytes / avg_launch_s / 1e9
+    traffic = measured_traffic(w.name)
+
+    decode = None
+    if args.decode_steps > 0 and w.dir_mode == 0:
+        s0 = sets[0]
+        st = states[0].clone()
+        ut = s0["u"][:, -1].contiguous()
+        dt_ = s0["delta"][:, -1].contiguous()
+        Bt = s0["B"][:, -1].contiguous()
+        Ct = s0["C"][:, -1].contiguous()
+        zt = s0["z"][:, -1].contiguous() if s0["z"] is not None else None
+        o = torch.empty_like(ut)
+        with torch.cuda.stream(stream):
+            for _ in range(10):
+                ms.scan_step(st, ut, dt_, s0["A"], Bt, Ct, s0["D"], zt, s0["delta_bias"], out=o, stream=stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.decode_steps):
+                ms.scan_step(st, ut, dt_, s0["A"], Bt, Ct, s0["D"], zt, s0["delta_bias"], out=o, stream=stream)
+            torch.cuda.synchronize()
+            dec_s = time.perf_counter() - t0
+        decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
+                  "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    rec = {
+        "metric": "scan elements (B*D*L*N)/s, selective scan forward, bf16 L=2048 D=1536 N=16",
+        "value": value,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) inputs, S4D-real A, %d input sets rotated)" % len(sets),
+        "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                   "dir_mode": ["fwd", "bwd", "bidir", "cross2d"][w.dir_mode], "gated": w.gated,
+                   "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": ach_elem, "peak": ALU_PEAK_ELEM / 1e9, "unit": "Gelem/s",
+                     "frac": ach_elem / (ALU_PEAK_ELEM / 1e9), "traffic": traffic,
+                     "kernel_avg_us": avg_launch_s * 1e6,
+                     "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
+                             "algorithmic_bytes": alg_bytes}},
+        "cpu_baseline": cpu,
+        "decode": decode,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

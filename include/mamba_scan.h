@@ -1,0 +1,154 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ * (libmamba_scan.so).
+ *
+ * The library computes the S6 selective scan of the Mamba layer and its
+ * bidirectional (Vision Mamba) and four-way cross-scan (VMamba SS2D) forms,
+ * plus a one-token recurrent step.  Sources, cited by page title and section:
+ *   [MFS] "从零理解 Mamba：选择性状态空间模型（Selective SSM）到 Mamba Block
+ *          （面向医学图像分割的基础铺垫）" (eutaboo.com)
+ *   [S4M] "从S4到Mamba：选择性状态空间模型的演进与革新" (jsqmd.com)
+ *   [MUN] "【临时文档---算法介绍】Mamba-UNet" (blog.csdn.net)
+ *   [VIM] "Vision Mamba：从状态空间模型到视觉革命的跨越" (x-humanoid.csdn.net)
+ *
+ * What one scan direction k computes for batch b and channel d, visiting the
+ * tokens t in that direction's order, with h[n] = 0 (or initial_state) before
+ * the first token:
+ *   Δ     = softplus(delta[t] + delta_bias[d])      [MFS §4.1 Algorithm 2; MUN §4]
+ *   Ā_n   = exp(Δ·A[d][n])                          [MFS §6.2 Step 4, eq (4)]
+ *   h[n]  = Ā_n·h[n] + Δ·B[t][n]·u[t]               [MFS §2.2 eq (2a); MUN §4: B̄ ≈ ΔB]
+ *   y_k   = Σ_n C[t][n]·h[n] + D[d]·u[t]            [MFS eq (2b); MUN §4: y = Ch + Dx]
+ * and the output is out[t] = (Σ_k y_k[t])·silu(z[t]) [MFS §6.2 Step 6; VIM §2.2].
+ *
+ * Conventions common to every entry point
+ *   - Every tensor is dense, row-major and C-contiguous, and indexed by token
+ *     position in the original (grid) order, never by scan order.
+ *   - All pointers are device pointers (HIP device memory) unless stated
+ *     otherwise.  The caller owns every buffer.  The library allocates no
+ *     memory, keeps no state between calls and is safe to call from several
+ *     host threads.  Calls on the same buffers must not overlap.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  The return
+ *     value reports host-side validation and launch errors only; faults during
+ *     execution surface at the next synchronisation of the stream.
+ *   - Device pointers must be 16-byte aligned.
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum {
+  MAMBA_OK = 0,
+  MAMBA_ERR_INVALID = -1,     /* NULL required pointer, size <= 0, L != H*W, unknown mode or dtype */
+  MAMBA_ERR_UNSUPPORTED = -2, /* valid but not built: N not a power of two in 1..64, dim not a
+                                 multiple of 8, a pointer not 16-byte aligned, a size too large
+                                 for 32-bit token indexing */
+  MAMBA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mamba_scan_fwd_workspace_bytes() */
+  MAMBA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+} mamba_status;
+
+/* Scan directions.  K is the number of directions each mode runs.
+ *   MAMBA_DIR_FWD      K=1: tokens 0..L-1.
+ *   MAMBA_DIR_BWD      K=1: tokens L-1..0.
+ *   MAMBA_DIR_BIDIR    K=2: k=0 forward, k=1 reversed, summed [VIM §2.2, VimBlock].
+ *   MAMBA_DIR_CROSS2D  K=4 over an H×W grid, token t = row*W + col [S4M §3, SS2D]:
+ *                      k=0 row-major, k=1 column-major (t = (p mod H)*W + p div H at
+ *                      scan position p), k=2 row-major reversed, k=3 column-major
+ *                      reversed; the four outputs are summed at each grid position. */
+typedef enum {
+  MAMBA_DIR_FWD = 0,
+  MAMBA_DIR_BWD = 1,
+  MAMBA_DIR_BIDIR = 2,
+  MAMBA_DIR_CROSS2D = 3
+} mamba_dir_mode;
+
+/* Element type of u, delta, z, B, C and out (A, D, delta_bias and states are
+ * always float32).  bf16 outputs are rounded to nearest, ties to even, once,
+ * after the direction sum and the gate. */
+typedef enum { MAMBA_DTYPE_F32 = 0, MAMBA_DTYPE_BF16 = 1 } mamba_dtype;
+
+/* Problem description shared by the entry points (host memory). */
+typedef struct {
+  int64_t batch;   /* B >= 1 */
+  int64_t dim;     /* D >= 1, the channel count (d_inner); a multiple of 8 */
+  int64_t seqlen;  /* L >= 1 tokens (ignored by mamba_scan_step) */
+  int64_t dstate;  /* N, state size per channel: 1, 2, 4, 8, 16, 32 or 64 */
+  int64_t height;  /* MAMBA_DIR_CROSS2D only: grid rows H, with H*W == L; else 0 */
+  int64_t width;   /* MAMBA_DIR_CROSS2D only: grid columns W; else 0 */
+  int32_t dtype;          /* mamba_dtype */
+  int32_t delta_softplus; /* 1: Δ = softplus(delta + bias); 0: Δ = delta + bias */
+  const float* initial_state; /* optional device pointer, [B][K][D][N] float32: state before
+                                 each direction's first token; NULL = zeros */
+  void* workspace;            /* device scratch owned by the caller (may be NULL when
+                                 mamba_scan_fwd_workspace_bytes() returns 0) */
+  size_t workspace_bytes;     /* size of workspace */
+} mamba_dims;
+
+/*
+ * Bytes of device workspace mamba_scan_fwd needs for these dims and mode
+ * (time-split carries of long sequences, per-direction partial outputs of
+ * the multi-direction modes).  A pure function of its arguments: it makes no
+ * HIP call.  Returns 0 when no workspace is needed, and (size_t)-1 when the
+ * arguments are invalid.  The workspace contents need not be initialised.
+ */
+size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
+
+/*
+ * Selective-scan forward pass [MFS §6.2 Step 4 and Step 6; VIM §2.2; S4M §3].
+ *
+ * Layouts (K from dir_mode; Ku = 1 for MAMBA_DIR_CROSS2D, whose four
+ * directions share u, else Ku = K; an axis of size 1 may be read as absent):
+ *   u           [B][Ku][L][D]  dtype
+ *   delta       [B][K][L][D]   dtype   (Δ before bias and softplus)
+ *   A           [K][D][N]      float32 (continuous-time diagonal A, normally < 0)
+ *   B, C        [B][K][L][N]   dtype   (input-dependent B_t, C_t)
+ *   D           [K][D]         float32 or NULL (no skip term)
+ *   z           [B][L][D]      dtype or NULL (no gate)
+ *   delta_bias  [K][D]         float32 or NULL (zero bias)
+ *   out         [B][L][D]      dtype, written; must not alias any input
+ *   last_state  [B][K][D][N]   float32 or NULL: the state after each
+ *                              direction's final scan step (for a reversed
+ *                              direction, after token 0)
+ * Errors: MAMBA_ERR_INVALID / _UNSUPPORTED / _WORKSPACE before any GPU work;
+ * MAMBA_ERR_HIP if a launch is rejected.
+ */
+int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                   int dir_mode, void* out, float* last_state, hipStream_t stream);
+
+/*
+ * One recurrent step of a forward scan (decode) [MFS §2.3: the recurrent form
+ * updates the state one token at a time].  For every batch b and channel d it
+ * applies the forward-scan update to `state` for one token and writes that
+ * token's gated output.
+ *   state        [B][D][N]  float32, read and updated in place (same layout as
+ *                           last_state of a MAMBA_DIR_FWD scan)
+ *   u_t, delta_t [B][D]     dtype
+ *   A            [D][N]     float32
+ *   B_t, C_t     [B][N]     dtype
+ *   D            [D]        float32 or NULL
+ *   z_t          [B][D]     dtype or NULL
+ *   delta_bias   [D]        float32 or NULL
+ *   out          [B][D]     dtype, written; must not alias any input
+ * dims->seqlen, height, width, initial_state and workspace are ignored.
+ */
+int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A,
+                    const void* B_t, const void* C_t, const float* D, const void* z_t,
+                    const float* delta_bias, const mamba_dims* dims, void* out, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* mamba_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

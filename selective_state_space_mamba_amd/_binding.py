@@ -1,0 +1,199 @@
+"""ctypes binding of libmamba_scan.so (declared in include/mamba_scan.h).
+
+Argument marshalling only: tensors become device pointers, shapes become a
+``mamba_dims`` struct, torch's current stream becomes the ``hipStream_t``.
+Every step of the scan runs in the library's HIP kernels; there is no
+fallback, and loading fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmamba_scan.so")
+
+MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP = 0, -1, -2, -3, -4
+DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+EXPORTED = ("mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step", "mamba_status_string")
+
+
+class MambaDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+        ("dstate", ctypes.c_int64), ("height", ctypes.c_int64), ("width", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("delta_softplus", ctypes.c_int32),
+        ("initial_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class MambaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, status_string(code), code))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (no build here; see selective_state_space_mamba_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libmamba_scan.so is not built (%s); run `python -m selective_state_space_mamba_amd.build` "
+                           "or __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.mamba_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.mamba_scan_fwd_workspace_bytes.argtypes = [ctypes.POINTER(MambaDims), i32]
+    lib.mamba_scan_fwd.restype = i32
+    lib.mamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), i32, vp, vp, vp]
+    lib.mamba_scan_step.restype = i32
+    lib.mamba_scan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), vp, vp]
+    lib.mamba_status_string.restype = ctypes.c_char_p
+    lib.mamba_status_string.argtypes = [i32]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().mamba_status_string(int(code)).decode()
+
+
+def num_dirs(dir_mode: int) -> int:
+    return {DIR_FWD: 1, DIR_BWD: 1, DIR_BIDIR: 2, DIR_CROSS2D: 4}[dir_mode]
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError("u/delta/B/C/z must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_dims(batch, dim, seqlen, dstate, dtype, *, height=0, width=0, delta_softplus=True,
+              initial_state=None, workspace=None, workspace_bytes=0) -> MambaDims:
+    return MambaDims(int(batch), int(dim), int(seqlen), int(dstate), int(height), int(width), int(dtype),
+                     1 if delta_softplus else 0, _ptr(initial_state), _ptr(workspace), int(workspace_bytes))
+
+
+def workspace_bytes(dims: MambaDims, dir_mode: int) -> int:
+    n = load_library().mamba_scan_fwd_workspace_bytes(ctypes.byref(dims), int(dir_mode))
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(MAMBA_ERR_INVALID, "mamba_scan_fwd_workspace_bytes")
+    return n
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0, width=0,
+             delta_softplus=True, initial_state=None, out=None, last_state=None, want_last_state=True,
+             workspace=None, stream=None):
+    """mamba_scan_fwd on torch tensors.
+
+    Shapes (K directions; the K axis is absent when K = 1; u has no K axis for
+    the cross scan): u [B][K][L][D], delta [B][K][L][D], A [K][D][N],
+    B/C [B][K][L][N], D/delta_bias [K][D], z [B][L][D].
+    Returns (out [B][L][D], last_state [B][K][D][N] or None)."""
+    import torch
+    lib = load_library()
+    K = num_dirs(dir_mode)
+    dev = u.device
+    dt = _dtype_code(u)
+    tdt = u.dtype
+    Bsz, L, Dm = delta.shape[0], delta.shape[-2], delta.shape[-1]
+    N = B.shape[-1]
+    kx = () if K == 1 else (K,)
+    ux = () if (K == 1 or dir_mode == DIR_CROSS2D) else (K,)
+    _check(u, "u", (Bsz,) + ux + (L, Dm), tdt, dev)
+    _check(delta, "delta", (Bsz,) + kx + (L, Dm), tdt, dev)
+    _check(B, "B", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(C, "C", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(z, "z", (Bsz, L, Dm), tdt, dev)
+    _check(A, "A", kx + (Dm, N), torch.float32, dev)
+    _check(D, "D", kx + (Dm,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", kx + (Dm,), torch.float32, dev)
+    _check(initial_state, "initial_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
+    if out is None:
+        out = torch.empty((Bsz, L, Dm), dtype=tdt, device=dev)
+    _check(out, "out", (Bsz, L, Dm), tdt, dev)
+    if last_state is None and want_last_state:
+        last_state = torch.empty((Bsz,) + kx + (Dm, N), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
+    dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
+                     initial_state=initial_state)
+    need = workspace_bytes(dims, dir_mode)
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        dims.workspace = workspace.data_ptr()
+        dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                            ctypes.byref(dims), int(dir_mode), _ptr(out), _ptr(last_state), _stream(stream))
+    if rc != MAMBA_OK:
+        raise MambaError(rc, "mamba_scan_fwd")
+    return out, last_state
+
+
+def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None, *, delta_softplus=True,
+              out=None, stream=None):
+    """mamba_scan_step on torch tensors: state [B][D][N] float32 (updated in
+    place), u_t/delta_t/z_t [B][D], B_t/C_t [B][N], A [D][N], D/delta_bias [D].
+    Returns out [B][D]."""
+    import torch
+    lib = load_library()
+    dev = u_t.device
+    dt = _dtype_code(u_t)
+    tdt = u_t.dtype
+    Bsz, Dm = u_t.shape
+    N = B_t.shape[-1]
+    _check(state, "state", (Bsz, Dm, N), torch.float32, dev)
+    for name, t, shp in (("delta_t", delta_t, (Bsz, Dm)), ("B_t", B_t, (Bsz, N)), ("C_t", C_t, (Bsz, N)),
+                         ("z_t", z_t, (Bsz, Dm))):
+        _check(t, name, shp, tdt, dev)
+    _check(A, "A", (Dm, N), torch.float32, dev)
+    _check(D, "D", (Dm,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (Dm,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((Bsz, Dm), dtype=tdt, device=dev)
+    _check(out, "out", (Bsz, Dm), tdt, dev)
+    dims = make_dims(Bsz, Dm, 1, N, dt, delta_softplus=delta_softplus)
+    rc = lib.mamba_scan_step(_ptr(state), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D),
+                             _ptr(z_t), _ptr(delta_bias), ctypes.byref(dims), _ptr(out), _stream(stream))
+    if rc != MAMBA_OK:
+        raise MambaError(rc, "mamba_scan_step")
+    return out

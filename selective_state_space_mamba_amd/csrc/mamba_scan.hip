@@ -1,0 +1,239 @@
+// mamba_scan.hip -- C ABI of the gfx950 selective-scan library: argument
+// validation, the launch plan, and kernel dispatch.  The kernels live in
+// scan_kernels.h; the interface is documented in include/mamba_scan.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mamba_scan.h"
+#include "scan_kernels.h"
+
+using namespace mscan;
+
+namespace {
+
+constexpr int kTile = 32;  // scan positions per LDS tile
+
+#ifndef MSCAN_TARGET_WAVES
+#define MSCAN_TARGET_WAVES 2048  // resident waves wanted before splitting sequences in time
+#endif
+#ifndef MSCAN_MIN_CHUNK
+#define MSCAN_MIN_CHUNK 1024     // shortest time chunk worth a separate aggregate pass
+#endif
+#ifndef MSCAN_MAX_CHUNKS
+#define MSCAN_MAX_CHUNKS 256
+#endif
+
+int num_dirs(int mode) { return mode == MAMBA_DIR_BIDIR ? 2 : mode == MAMBA_DIR_CROSS2D ? 4 : 1; }
+
+// 2-bit traversal kind of each direction.
+int kinds_of(int mode) {
+  switch (mode) {
+    case MAMBA_DIR_FWD: return KIND_ROW_FWD;
+    case MAMBA_DIR_BWD: return KIND_ROW_REV;
+    case MAMBA_DIR_BIDIR: return KIND_ROW_FWD | (KIND_ROW_REV << 2);
+    default: return KIND_ROW_FWD | (KIND_COL_FWD << 2) | (KIND_ROW_REV << 4) | (KIND_COL_REV << 6);
+  }
+}
+
+// States per lane for a state size N (waves per workgroup = N / G).
+int states_per_lane(int64_t N) { return N <= 4 ? (int)N : N <= 16 ? 4 : (int)(N / 4); }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {
+  int K, Ku, nblk_d, nchunks, chunk_len;
+  size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
+  size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
+};
+
+// Validates the sizes (no pointers) and derives the launch plan.  A pure
+// function of dims and mode.
+int make_plan(const mamba_dims* g, int mode, Plan* pl) {
+  if (!g) return MAMBA_ERR_INVALID;
+  if (mode < MAMBA_DIR_FWD || mode > MAMBA_DIR_CROSS2D) return MAMBA_ERR_INVALID;
+  if (g->dtype != MAMBA_DTYPE_F32 && g->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID;
+  if (g->batch <= 0 || g->dim <= 0 || g->seqlen <= 0 || g->dstate <= 0) return MAMBA_ERR_INVALID;
+  if (mode == MAMBA_DIR_CROSS2D &&
+      (g->height <= 0 || g->width <= 0 || g->height > INT32_MAX || g->width > INT32_MAX ||
+       g->height * g->width != g->seqlen))
+    return MAMBA_ERR_INVALID;
+  const int64_t N = g->dstate;
+  if (N > 64 || (N & (N - 1)) != 0) return MAMBA_ERR_UNSUPPORTED;
+  if (g->dim % 8 != 0) return MAMBA_ERR_UNSUPPORTED;
+  const int K = num_dirs(mode);
+  // token and grid indices are 32-bit inside the kernels; element offsets are 64-bit
+  if (g->seqlen > INT32_MAX / 2 || g->dim > INT32_MAX / 2 || g->batch > INT32_MAX / 8 ||
+      g->batch * g->dim > INT32_MAX / 4)
+    return MAMBA_ERR_UNSUPPORTED;
+  pl->K = K;
+  pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
+  pl->nblk_d = (int)((g->dim + 63) / 64);
+  const int64_t nw = (int64_t)K * g->batch * pl->nblk_d * (N / states_per_lane(N));
+  const int64_t L = g->seqlen;
+  int64_t nch = 1;
+  if (nw < MSCAN_TARGET_WAVES && L >= 2 * MSCAN_MIN_CHUNK) {
+    nch = (MSCAN_TARGET_WAVES + nw - 1) / nw;
+    if (nch > L / MSCAN_MIN_CHUNK) nch = L / MSCAN_MIN_CHUNK;
+    if (nch > MSCAN_MAX_CHUNKS) nch = MSCAN_MAX_CHUNKS;
+  }
+  int64_t clen = (L + nch - 1) / nch;
+  clen = (clen + kTile - 1) / kTile * kTile;
+  nch = (L + clen - 1) / clen;
+  if (pl->nblk_d * nch * g->batch * K > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  pl->nchunks = (int)nch;
+  pl->chunk_len = (int)clen;
+  const size_t al = 256;
+  auto up = [&](size_t x) { return (x + al - 1) / al * al; };
+  pl->ws_y_bytes = K > 1 ? up((size_t)K * g->batch * L * g->dim * sizeof(float)) : 0;
+  pl->agg_state_bytes = nch > 1 ? up((size_t)K * g->batch * (nch - 1) * g->dim * N * sizeof(float)) : 0;
+  pl->agg_dsum_bytes = nch > 1 ? up((size_t)K * g->batch * (nch - 1) * g->dim * sizeof(float)) : 0;
+  return MAMBA_OK;
+}
+
+template <typename TIn, int N>
+int launch_scan(const ScanParams& base, const Plan& pl, hipStream_t stream) {
+  constexpr int G = N <= 4 ? N : N <= 16 ? 4 : N / 4;
+  constexpr int NT = 64 * (N / G);
+  ScanParams p = base;
+  if (pl.nchunks > 1) {
+    p.grid_chunks = pl.nchunks - 1;
+    const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, G, kTile, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  p.grid_chunks = pl.nchunks;
+  const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
+  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, G, kTile, false>), dim3(blocks), dim3(NT), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  if (p.ws_y) {
+    const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
+    const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
+    hipLaunchKernelGGL((merge_dirs_kernel<TIn>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
+                       static_cast<const TIn*>(p.z), static_cast<TIn*>(p.out), p.K, rows8,
+                       (int64_t)p.Bsz * p.L * p.Dm);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  return MAMBA_OK;
+}
+
+template <typename TIn>
+int dispatch_scan(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s) {
+  switch (N) {
+    case 1: return launch_scan<TIn, 1>(p, pl, s);
+    case 2: return launch_scan<TIn, 2>(p, pl, s);
+    case 4: return launch_scan<TIn, 4>(p, pl, s);
+    case 8: return launch_scan<TIn, 8>(p, pl, s);
+    case 16: return launch_scan<TIn, 16>(p, pl, s);
+    case 32: return launch_scan<TIn, 32>(p, pl, s);
+    case 64: return launch_scan<TIn, 64>(p, pl, s);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+
+template <typename TIn, int N>
+int launch_step(const StepParams& p, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((p.Bsz * p.Dm + 255) / 256);
+  hipLaunchKernelGGL((scan_step_kernel<TIn, N>), dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TIn>
+int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
+  switch (N) {
+    case 1: return launch_step<TIn, 1>(p, s);
+    case 2: return launch_step<TIn, 2>(p, s);
+    case 4: return launch_step<TIn, 4>(p, s);
+    case 8: return launch_step<TIn, 8>(p, s);
+    case 16: return launch_step<TIn, 16>(p, s);
+    case 32: return launch_step<TIn, 32>(p, s);
+    case 64: return launch_step<TIn, 64>(p, s);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_mode) {
+  Plan pl;
+  if (make_plan(dims, dir_mode, &pl) != MAMBA_OK) return (size_t)-1;
+  return pl.total();
+}
+
+int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                   int dir_mode, void* out, float* last_state, hipStream_t stream) {
+  Plan pl;
+  const int rc = make_plan(dims, dir_mode, &pl);
+  if (rc != MAMBA_OK) return rc;
+  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, out, last_state, dims->initial_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
+  const size_t need = pl.total();
+  if (need > 0 && (!dims->workspace || dims->workspace_bytes < need || !aligned16(dims->workspace)))
+    return MAMBA_ERR_WORKSPACE;
+
+  ScanParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.delta_bias = delta_bias;
+  p.init_state = dims->initial_state;
+  p.out = out;
+  char* ws = static_cast<char*>(dims->workspace);
+  p.ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
+  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
+  p.last_state = last_state;
+  p.Bsz = (int)dims->batch;
+  p.Dm = (int)dims->dim;
+  p.L = (int)dims->seqlen;
+  p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
+  p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
+  p.K = pl.K;
+  p.Ku = pl.Ku;
+  p.kinds = kinds_of(dir_mode);
+  p.nchunks = pl.nchunks;
+  p.chunk_len = pl.chunk_len;
+  p.nblk_d = pl.nblk_d;
+  p.softplus = dims->delta_softplus ? 1 : 0;
+  if (dims->dtype == MAMBA_DTYPE_BF16) return dispatch_scan<uint16_t>(dims->dstate, p, pl, stream);
+  return dispatch_scan<float>(dims->dstate, p, pl, stream);
+}
+
+int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A, const void* B_t,
+                    const void* C_t, const float* D, const void* z_t, const float* delta_bias,
+                    const mamba_dims* dims, void* out, hipStream_t stream) {
+  if (!dims || !state || !u_t || !delta_t || !A || !B_t || !C_t || !out) return MAMBA_ERR_INVALID;
+  if (dims->dtype != MAMBA_DTYPE_F32 && dims->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->dstate <= 0) return MAMBA_ERR_INVALID;
+  const int64_t N = dims->dstate;
+  if (N > 64 || (N & (N - 1)) != 0) return MAMBA_ERR_UNSUPPORTED;
+  if (dims->dim % 8 != 0 || dims->batch * dims->dim > INT32_MAX / 64) return MAMBA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, out};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
+  StepParams p{state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, out,
+               (int)dims->batch, (int)dims->dim, dims->delta_softplus ? 1 : 0};
+  if (dims->dtype == MAMBA_DTYPE_BF16) return dispatch_step<uint16_t>(N, p, stream);
+  return dispatch_step<float>(N, p, stream);
+}
+
+const char* mamba_status_string(int status) {
+  switch (status) {
+    case MAMBA_OK: return "ok";
+    case MAMBA_ERR_INVALID: return "invalid argument (null pointer, non-positive size, L != H*W, or unknown mode/dtype)";
+    case MAMBA_ERR_UNSUPPORTED: return "unsupported (state size, channel count, alignment or size limit)";
+    case MAMBA_ERR_WORKSPACE: return "workspace missing or smaller than mamba_scan_fwd_workspace_bytes()";
+    case MAMBA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+"""Shared helpers of the GPU parity tests: moving the seeded numpy inputs to the
+GPU, running the library through its C ABI, running the oracle, and the
+tolerance checks.
+
+Tolerances (written once here; the scan's floating-point results differ from
+the fp64 oracle by rounding only):
+  * float32 inputs:  max_i |o_i - r_i| / max_i |r_i|  <= 2e-4
+  * bfloat16 inputs: max_i |o_i - r_i| / max_i |r_i|  <= 1e-2  and
+                     ||o - r||_2 / ||r||_2             <= 3e-3
+The output rounding to bfloat16 alone contributes up to 2^-9 of the maximum
+and about 2^-9/sqrt(3) in the L2 ratio.  The error is measured normwise
+because many outputs of N(0,1) data lie near zero, where an elementwise
+relative error says nothing about accuracy.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import selective_state_space_mamba_amd as ms
+from selective_state_space_mamba_amd import inputs as I
+
+TOL = {"f32": dict(max=2e-4, l2=2e-4), "bf16": dict(max=1e-2, l2=3e-3)}
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def to_dev(x):
+    """numpy (float32, or uint16 bf16 bits) -> torch tensor on cuda:0."""
+    t = torch()
+    if x is None:
+        return None
+    if x.dtype == np.uint16:
+        return t.from_numpy(x.view(np.int16)).to("cuda:0").view(t.bfloat16)
+    return t.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+def from_dev(t_):
+    """torch tensor (float32 or bf16) -> numpy float64."""
+    t = torch()
+    if t_.dtype == t.bfloat16:
+        bits = t_.view(t.int16).cpu().numpy().view(np.uint16)
+        return I.bf16_to_f32(bits).astype(np.float64)
+    return t_.float().cpu().numpy().astype(np.float64)
+
+
+def dev_inputs(x):
+    return {k: to_dev(v) for k, v in x.items()}
+
+
+def gpu_fwd(w: I.Workload, xd: dict, **kw):
+    """Run mamba_scan_fwd on device inputs; returns (out, last_state) as torch tensors."""
+    out, st = ms.scan_fwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd.get("D"), xd.get("z"),
+                          xd.get("delta_bias"), dir_mode=w.dir_mode, height=w.height, width=w.width, **kw)
+    torch().cuda.synchronize()
+    return out, st
+
+
+def oracle_fwd(w: I.Workload, x: dict, rows=None, **kw):
+    return oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x.get("D"), x.get("z"), x.get("delta_bias"),
+                       dir_mode=w.dir_mode, height=w.height, width=w.width, rows=rows, **kw)
+
+
+def errors(got, want):
+    got = np.asarray(got, np.float64).ravel()
+    want = np.asarray(want, np.float64).ravel()
+    scale = np.max(np.abs(want))
+    emax = np.max(np.abs(got - want)) / scale if scale > 0 else np.max(np.abs(got - want))
+    nr = np.linalg.norm(want)
+    el2 = np.linalg.norm(got - want) / nr if nr > 0 else np.linalg.norm(got - want)
+    return float(emax), float(el2)
+
+
+def assert_close(name, got, want, dtype):
+    assert np.all(np.isfinite(got)), "%s: non-finite values in the GPU result" % name
+    emax, el2 = errors(got, want)
+    tol = TOL[dtype]
+    print("%s: normwise max err %.3e (tol %.0e), L2 err %.3e (tol %.0e)" % (name, emax, tol["max"], el2, tol["l2"]),
+          flush=True)
+    assert emax <= tol["max"] and el2 <= tol["l2"], (name, emax, el2)
+
+
+def sample_rows(rng, batch, dim, n):
+    """n distinct (b, d) rows, always including the first and last channel."""
+    rows = {(0, 0), (batch - 1, dim - 1)}
+    while len(rows) < min(n, batch * dim):
+        rows.add((int(rng.integers(batch)), int(rng.integers(dim))))
+    return np.array(sorted(rows), dtype=np.int64)

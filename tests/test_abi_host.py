@@ -1,0 +1,102 @@
+"""Host-side checks of the C ABI (no GPU work): the library loads, exports every
+function include/mamba_scan.h declares, sizes its workspace as a pure
+function of the problem, and rejects invalid calls before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_mamba_amd as ms
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # 16-byte aligned stand-in pointer: every call below fails validation first
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mamba_scan.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ms.LIB_PATH):
+        from selective_state_space_mamba_amd import build
+        build.build(force=False)
+    return ms.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert declared == sorted(ms.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert len(ms.status_string(code)) > 0
+    assert ms.status_string(0) == "ok"
+
+
+def dims(**kw):
+    base = dict(batch=2, dim=64, seqlen=100, dstate=16, dtype=ms.DTYPE_BF16)
+    base.update(kw)
+    return ms.make_dims(base.pop("batch"), base.pop("dim"), base.pop("seqlen"), base.pop("dstate"),
+                        base.pop("dtype"), **base)
+
+
+def test_workspace_bytes_pure_function(lib):
+    assert ms.workspace_bytes(dims(), ms.DIR_FWD) == 0  # short sequence, enough rows: no split
+    bi = ms.workspace_bytes(dims(), ms.DIR_BIDIR)
+    assert bi >= 2 * 2 * 100 * 64 * 4  # per-direction fp32 rows
+    assert ms.workspace_bytes(dims(), ms.DIR_BIDIR) == bi
+    cross = ms.workspace_bytes(dims(seqlen=96, height=8, width=12), ms.DIR_CROSS2D)
+    assert cross >= 4 * 2 * 96 * 64 * 4
+    # a long sequence with few rows is split in time: aggregate state + ΣΔ per chunk
+    long = ms.workspace_bytes(dims(batch=1, seqlen=1 << 16), ms.DIR_FWD)
+    assert long > 0 and long % 256 == 0
+    with pytest.raises(ms.MambaError):
+        ms.workspace_bytes(dims(seqlen=0), ms.DIR_FWD)
+
+
+def call_fwd(lib, d, mode=ms.DIR_FWD, **ptrs):
+    p = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, out=FAKE, last=None)
+    p.update(ptrs)
+    return lib.mamba_scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"],
+                              ctypes.byref(d), mode, p["out"], p["last"], None)
+
+
+def test_fwd_validation(lib):
+    assert call_fwd(lib, dims(), u=None) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(), out=None) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(batch=0)) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(seqlen=-3)) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(dtype=5)) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(), mode=9) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(seqlen=96, height=8, width=11), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(seqlen=96), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
+    assert call_fwd(lib, dims(dstate=12)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(dstate=128)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(dim=60)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(), u=FAKE + 4) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(), z=FAKE + 2) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    # multi-direction modes need the workspace
+    assert call_fwd(lib, dims(), mode=ms.DIR_BIDIR) == ms._binding.MAMBA_ERR_WORKSPACE
+    d = dims(workspace=FAKE, workspace_bytes=16)
+    assert call_fwd(lib, d, mode=ms.DIR_BIDIR) == ms._binding.MAMBA_ERR_WORKSPACE
+
+
+def test_step_validation(lib):
+    def step(d, **ptrs):
+        p = dict(state=FAKE, u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, out=FAKE)
+        p.update(ptrs)
+        return lib.mamba_scan_step(p["state"], p["u"], p["delta"], p["A"], p["B"], p["C"], None, None, None,
+                                   ctypes.byref(d), p["out"], None)
+    assert step(dims(), state=None) == ms._binding.MAMBA_ERR_INVALID
+    assert step(dims(dim=0)) == ms._binding.MAMBA_ERR_INVALID
+    assert step(dims(dstate=3)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert step(dims(), B=FAKE + 8) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert lib.mamba_scan_step(None, None, None, None, None, None, None, None, None, None, None, None) == \
+        ms._binding.MAMBA_ERR_INVALID

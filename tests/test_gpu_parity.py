@@ -1,0 +1,299 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs, plus properties that hold at any size.
+
+Small cases span several 64-channel blocks and 32-step tiles with ragged
+tails, every direction mode, every supported state size, the time-split path,
+and the optional arguments.  The five specified workloads run at full size in
+the launch configuration the benchmark times, checked on sampled (b, d) rows
+that the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import selective_state_space_mamba_amd as ms
+from selective_state_space_mamba_amd import inputs as I
+
+from scanutil import (TOL, assert_close, dev_inputs, errors, from_dev, gpu_fwd, oracle_fwd, sample_rows, to_dev,
+                      torch)
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    ms.load_library()  # fails loudly when the HIP library is missing
+    yield
+
+
+def announce(msg):
+    print("[gpu case] " + msg, flush=True)
+
+
+def run_and_check(w, x=None, name=None, **kw):
+    x = x if x is not None else I.make_inputs(w)
+    announce("%s %s" % (name or w.name, w))
+    out, st = gpu_fwd(w, dev_inputs(x), **kw)
+    ref_out, ref_st = oracle_fwd(w, x, **{k: v for k, v in kw.items() if k in ("delta_softplus",)},
+                                 initial_state=(None if kw.get("initial_state") is None
+                                                else kw["initial_state"].cpu().numpy()))
+    assert_close((name or w.name) + " out", from_dev(out), ref_out, w.dtype)
+    if st is not None:
+        assert_close((name or w.name) + " last_state", from_dev(st), ref_st.reshape(from_dev(st).shape),
+                     "f32" if w.dtype == "f32" else "bf16")
+    return out, st, ref_out, ref_st
+
+
+# ---------------------------------------------------------------------------------------------
+# the tiny float32 workload, also against the stored oracle fixture
+
+def test_tiny_f32_workload():
+    w = I.WORKLOADS["tiny_f32"]
+    out, st, ref_out, ref_st = run_and_check(w)
+    want = np.loadtxt(os.path.join(GOLDEN, "tiny_f32_oracle.txt"))
+    got = np.concatenate([from_dev(out).ravel(), from_dev(st).ravel()])
+    emax, _ = errors(got[:out.numel()], want[:out.numel()])
+    assert emax <= TOL["f32"]["max"]
+
+
+SMALL = {
+    "fwd_bf16_ragged": I.Workload("fwd_bf16_ragged", 2, 136, 300, 16, I.DIR_FWD, "bf16", True, 11),
+    "fwd_f32_ragged": I.Workload("fwd_f32_ragged", 2, 136, 300, 16, I.DIR_FWD, "f32", True, 12),
+    "bwd_bf16": I.Workload("bwd_bf16", 2, 72, 133, 16, I.DIR_BWD, "bf16", True, 13),
+    "bwd_f32": I.Workload("bwd_f32", 1, 64, 77, 16, I.DIR_BWD, "f32", False, 14),
+    "bidir_bf16": I.Workload("bidir_bf16", 3, 72, 197, 16, I.DIR_BIDIR, "bf16", True, 15),
+    "bidir_f32": I.Workload("bidir_f32", 2, 16, 45, 4, I.DIR_BIDIR, "f32", True, 16),
+    "cross2d_bf16": I.Workload("cross2d_bf16", 2, 64, 240, 16, I.DIR_CROSS2D, "bf16", False, 17, 12, 20),
+    "cross2d_f32_gated": I.Workload("cross2d_f32_gated", 1, 16, 35, 8, I.DIR_CROSS2D, "f32", True, 18, 5, 7),
+    "cross2d_tall_f32": I.Workload("cross2d_tall_f32", 1, 24, 66, 4, I.DIR_CROSS2D, "f32", False, 19, 33, 2),
+    "split_fwd_bf16": I.Workload("split_fwd_bf16", 1, 64, 4133, 16, I.DIR_FWD, "bf16", True, 20),
+    "split_fwd_f32": I.Workload("split_fwd_f32", 1, 72, 5000, 16, I.DIR_FWD, "f32", True, 21),
+    "split_bwd_bf16": I.Workload("split_bwd_bf16", 1, 64, 3001, 16, I.DIR_BWD, "bf16", True, 22),
+    "split_bidir_bf16": I.Workload("split_bidir_bf16", 1, 64, 3000, 16, I.DIR_BIDIR, "bf16", True, 23),
+    "split_cross2d_bf16": I.Workload("split_cross2d_bf16", 1, 32, 2304, 16, I.DIR_CROSS2D, "bf16", False, 24, 48, 48),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_workloads(name):
+    run_and_check(SMALL[name])
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8, 32, 64])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_state_sizes(N, dtype):
+    w = I.Workload("N%d_%s" % (N, dtype), 2, 80, 70, N, I.DIR_FWD, dtype, True, 100 + N)
+    run_and_check(w)
+
+
+def test_state_size_64_bidir():
+    run_and_check(I.Workload("N64_bidir", 1, 64, 50, 64, I.DIR_BIDIR, "f32", True, 131))
+
+
+def test_options_softplus_off_no_skip_no_gate_no_bias():
+    w = I.Workload("opts", 2, 64, 90, 16, I.DIR_FWD, "f32", False, 31)
+    x = I.make_inputs(w)
+    x["delta"] = np.abs(x["delta"]) * np.float32(0.1)  # softplus off: keep Δ positive and small
+    x["D"] = None
+    x["delta_bias"] = None
+    run_and_check(w, x, name="softplus_off", delta_softplus=False)
+
+
+def test_initial_state():
+    for mode, K in ((I.DIR_FWD, 1), (I.DIR_BIDIR, 2)):
+        w = I.Workload("init", 2, 72, 150, 16, mode, "bf16", True, 32)
+        x = I.make_inputs(w)
+        r = np.random.Generator(np.random.PCG64(5))
+        shape = (2, 72, 16) if K == 1 else (2, K, 72, 16)
+        init = r.standard_normal(shape).astype(np.float32)
+        run_and_check(w, x, name="init_state_%d" % mode, initial_state=to_dev(init))
+    # and through the time-split path
+    w = I.Workload("init_split", 1, 64, 3000, 16, I.DIR_FWD, "bf16", True, 33)
+    init = np.random.Generator(np.random.PCG64(6)).standard_normal((1, 64, 16)).astype(np.float32)
+    run_and_check(w, I.make_inputs(w), name="init_state_split", initial_state=to_dev(init))
+
+
+def test_no_last_state():
+    w = I.Workload("nolast", 1, 64, 64, 16, I.DIR_FWD, "bf16", True, 34)
+    x = I.make_inputs(w)
+    out, st = ms.scan_fwd(*[to_dev(x[k]) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")],
+                          want_last_state=False)
+    torch().cuda.synchronize()
+    assert st is None
+    ref, _ = oracle_fwd(w, x)
+    assert_close("nolast", from_dev(out), ref, "bf16")
+
+
+# ---------------------------------------------------------------------------------------------
+# exact properties
+
+def test_bf16_output_is_round_to_nearest_even():
+    """C = 0, D = 1.5, no gate: out = bf16(1.5·u), where 1.5·u is exact in fp32 and
+    often a tie at bf16 precision, so the rounding mode is visible bit for bit."""
+    w = I.Workload("rne", 1, 64, 96, 4, I.DIR_FWD, "bf16", False, 41)
+    x = I.make_inputs(w)
+    x["C"] = np.zeros_like(x["C"])
+    x["D"] = np.full_like(x["D"], 1.5)
+    announce("rne")
+    out, _ = gpu_fwd(w, dev_inputs(x))
+    got = out.view(torch().int16).cpu().numpy().view(np.uint16)
+    want = I.bf16_bits(I.bf16_to_f32(x["u"]) * np.float32(1.5))
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("mode,K", [(I.DIR_FWD, 1), (I.DIR_BWD, 1), (I.DIR_BIDIR, 2), (I.DIR_CROSS2D, 4)])
+def test_one_hot_state_layout(mode, K):
+    """A single u = 1 at the first scan position of one (b, k, d) row and B = e_n:
+    last_state is nonzero exactly at [b, k, d, n]."""
+    Bsz, H, W, Dm, N = 2, 6, 8, 72, 16
+    L = H * W
+    r = np.random.Generator(np.random.PCG64(42 + mode))
+    Ku = 1 if mode == I.DIR_CROSS2D else K
+    for trial in range(2):
+        bs, ks, ds, ns = int(r.integers(Bsz)), int(r.integers(K)), int(r.integers(Dm)), int(r.integers(N))
+        first = oracle.token(mode, ks, 0, L, H, W)
+        u = np.zeros((Bsz, Ku, L, Dm), np.float32)
+        u[bs, 0 if Ku == 1 else ks, first, ds] = 1.0
+        delta = r.uniform(0.05, 0.3, (Bsz, K, L, Dm)).astype(np.float32)
+        B = np.zeros((Bsz, K, L, N), np.float32)
+        B[bs, ks, first, ns] = 1.0
+        C = r.standard_normal((Bsz, K, L, N)).astype(np.float32)
+        A = -r.uniform(0.5, 2, (K, Dm, N)).astype(np.float32)
+        sq = lambda a: a.reshape(a.shape[:1] + a.shape[2:]) if a.shape[1] == 1 else a
+        x = dict(u=sq(u), delta=sq(delta), B=sq(B), C=sq(C), A=A[0] if K == 1 else A)
+        w = I.Workload("onehot", Bsz, Dm, L, N, mode, "f32", False, 0, H if mode == I.DIR_CROSS2D else 0,
+                       W if mode == I.DIR_CROSS2D else 0)
+        announce("one-hot mode %d trial %d" % (mode, trial))
+        _, st = gpu_fwd(w, dev_inputs(x), delta_softplus=False)
+        st = st.cpu().numpy().reshape(Bsz, K, Dm, N)
+        nz = np.argwhere(st != 0)
+        assert nz.tolist() == [[bs, ks, ds, ns]]
+        _, ref = oracle_fwd(w, x, delta_softplus=False)
+        assert abs(st[bs, ks, ds, ns] - ref[bs, ks, ds, ns]) <= 2e-6 * abs(ref[bs, ks, ds, ns])
+
+
+def test_reversed_scan_is_flipped_forward_bitwise():
+    w = I.Workload("flip", 2, 72, 150, 16, I.DIR_FWD, "bf16", True, 43)
+    x = I.make_inputs(w)
+    flip = lambda a: np.ascontiguousarray(a[:, ::-1])
+    xf = dict(x, u=flip(x["u"]), delta=flip(x["delta"]), B=flip(x["B"]), C=flip(x["C"]), z=flip(x["z"]))
+    announce("flip")
+    fo, fs = gpu_fwd(w, dev_inputs(xf))
+    bo, bs = gpu_fwd(w.with_(dir_mode=I.DIR_BWD), dev_inputs(x))
+    np.testing.assert_array_equal(bo.flip(1).cpu().view(torch().int16).numpy(), fo.cpu().view(torch().int16).numpy())
+    np.testing.assert_array_equal(bs.cpu().numpy(), fs.cpu().numpy())
+
+
+def test_repeatable_overwrites_everything_and_stays_in_bounds():
+    t = torch()
+    for w in (SMALL["fwd_bf16_ragged"], SMALL["bidir_bf16"], SMALL["cross2d_bf16"], SMALL["split_fwd_bf16"]):
+        x = I.make_inputs(w)
+        xd = dev_inputs(x)
+        announce("poison/guard %s" % w.name)
+        Bsz, L, Dm, N, K = w.batch, w.seqlen, w.dim, w.dstate, w.ndirs
+        guard = 4096
+        ob = t.full((Bsz * L * Dm + guard,), float("nan"), dtype=t.bfloat16, device="cuda:0")
+        sb = t.full((Bsz * K * Dm * N + guard,), float("nan"), dtype=t.float32, device="cuda:0")
+        out = ob[:Bsz * L * Dm].view(Bsz, L, Dm)
+        st = sb[:Bsz * K * Dm * N].view((Bsz, Dm, N) if K == 1 else (Bsz, K, Dm, N))
+        ms.scan_fwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd["D"], xd["z"], xd["delta_bias"],
+                    dir_mode=w.dir_mode, height=w.height, width=w.width, out=out, last_state=st)
+        t.cuda.synchronize()
+        assert not t.isnan(out).any() and not t.isnan(st).any()
+        assert t.isnan(ob[Bsz * L * Dm:]).all() and t.isnan(sb[Bsz * K * Dm * N:]).all()
+        first = (out.clone(), st.clone())
+        ms.scan_fwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd["D"], xd["z"], xd["delta_bias"],
+                    dir_mode=w.dir_mode, height=w.height, width=w.width, out=out, last_state=st)
+        t.cuda.synchronize()
+        assert t.equal(out.view(t.int16), first[0].view(t.int16)) and t.equal(st, first[1])
+
+
+def test_cross_scan_transpose_symmetry():
+    """H = W: transposing the grid swaps directions 0<->1 and 2<->3."""
+    w = I.Workload("tr", 1, 64, 144, 16, I.DIR_CROSS2D, "f32", True, 44, 12, 12)
+    x = I.make_inputs(w)
+    H = 12
+    T = lambda a: np.ascontiguousarray(a.reshape(a.shape[:-2] + (H, H, a.shape[-1])).swapaxes(-3, -2).reshape(a.shape))
+    perm = [1, 0, 3, 2]
+    xt = dict(u=T(x["u"]), delta=T(x["delta"][:, perm]), B=T(x["B"][:, perm]), C=T(x["C"][:, perm]),
+              z=T(x["z"]), A=np.ascontiguousarray(x["A"][perm]), D=np.ascontiguousarray(x["D"][perm]),
+              delta_bias=np.ascontiguousarray(x["delta_bias"][perm]))
+    announce("transpose")
+    o1, s1 = gpu_fwd(w, dev_inputs(x))
+    o2, s2 = gpu_fwd(w, dev_inputs(xt))
+    assert_close("transpose out", from_dev(o2), T(from_dev(o1)), "f32")
+    assert_close("transpose state", from_dev(s2), from_dev(s1)[:, perm], "f32")
+
+
+# ---------------------------------------------------------------------------------------------
+# decode step
+
+def run_decode(w, L0, steps, rows=None):
+    x = I.make_inputs(w, seqlen=L0 + steps)
+    head = {k: (v[:, :L0] if k in ("u", "delta", "B", "C", "z") else v) for k, v in x.items()}
+    xd = dev_inputs({k: (np.ascontiguousarray(v) if v is not None else None) for k, v in head.items()})
+    announce("decode %s L0=%d steps=%d" % (w.name, L0, steps))
+    _, st = gpu_fwd(w.with_(seqlen=L0), xd)
+    state = st.contiguous()
+    # step-major copies so that each step's [B][D] / [B][N] slice is contiguous
+    tail = {k: to_dev(np.ascontiguousarray(x[k][:, L0:].swapaxes(0, 1))) for k in ("u", "delta", "B", "C", "z")}
+    outs = []
+    for s in range(steps):
+        outs.append(ms.scan_step(state, tail["u"][s], tail["delta"][s], xd["A"], tail["B"][s],
+                                 tail["C"][s], xd["D"], tail["z"][s], xd["delta_bias"]))
+    torch().cuda.synchronize()
+    got = np.stack([from_dev(o) for o in outs], axis=1)  # [B][steps][D]
+    ref_out, ref_st = oracle_fwd(w.with_(seqlen=L0 + steps), x, rows=rows)
+    return got, from_dev(state), ref_out, ref_st
+
+
+def test_decode_continues_scan_small():
+    w = I.Workload("dec", 2, 72, 0, 16, I.DIR_FWD, "bf16", True, 51)
+    got, st, ref_out, ref_st = run_decode(w, 100, 40)
+    assert_close("decode out", got, ref_out[:, 100:], "bf16")
+    assert_close("decode state", st, ref_st[:, 0], "bf16")
+    wf = I.Workload("decf", 1, 16, 0, 4, I.DIR_FWD, "f32", True, 52)
+    got, st, ref_out, ref_st = run_decode(wf, 64, 16)
+    assert_close("decode f32 out", got, ref_out[:, 64:], "f32")
+    assert_close("decode f32 state", st, ref_st[:, 0], "f32")
+
+
+# ---------------------------------------------------------------------------------------------
+# the specified workloads at full size, sampled rows
+
+def full_size_check(w, nrows=48, seed=7):
+    x = I.make_inputs(w)
+    announce("full-size %s" % w.name)
+    out, st = gpu_fwd(w, dev_inputs(x))
+    rows = sample_rows(np.random.Generator(np.random.PCG64(seed)), w.batch, w.dim, nrows)
+    ref_out, ref_st = oracle_fwd(w, x, rows=rows)
+    o = from_dev(out)
+    s = from_dev(st).reshape(w.batch, w.ndirs, w.dim, w.dstate)
+    got_o = np.stack([o[b, :, d] for b, d in rows])
+    got_s = np.stack([s[b, :, d] for b, d in rows])
+    assert_close(w.name + " out (sampled rows)", got_o, ref_out, w.dtype)
+    assert_close(w.name + " last_state (sampled rows)", got_s, ref_st, w.dtype)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mamba130m_layer", "long_context", "vim_bidir_224", "vim_bidir_1248",
+                                  "vmamba_ss2d"])
+def test_full_size_workloads(name):
+    full_size_check(I.WORKLOADS[name])
+
+
+@pytest.mark.slow
+def test_full_size_decode_512_steps():
+    w = I.WORKLOADS["mamba130m_layer"]
+    rows = sample_rows(np.random.Generator(np.random.PCG64(8)), w.batch, w.dim, 32)
+    got, st, ref_out, ref_st = run_decode(w, w.seqlen, I.DECODE_STEPS, rows=rows)
+    got_rows = np.stack([got[b, :, d] for b, d in rows])
+    st_rows = np.stack([st[b, d] for b, d in rows])
+    assert_close("decode512 out (sampled rows)", got_rows, ref_out[:, w.seqlen:], "bf16")
+    assert_close("decode512 state (sampled rows)", st_rows, ref_st[:, 0], "bf16")
