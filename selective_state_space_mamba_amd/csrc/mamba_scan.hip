@@ -11,10 +11,19 @@ using namespace mscan;
 
 namespace {
 
-constexpr int kTile = 32;  // scan positions per LDS tile
+#ifndef MSCAN_TILE
+#define MSCAN_TILE 32
+#endif
+constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 
 #ifndef MSCAN_TARGET_WAVES
-#define MSCAN_TARGET_WAVES 2048  // resident waves wanted before splitting sequences in time
+#define MSCAN_TARGET_WAVES 3072  // resident waves wanted: 3 per SIMD (one wave issues VALU at half rate)
+#endif
+#ifndef MSCAN_FORCE_LAYOUT
+#define MSCAN_FORCE_LAYOUT -1
+#endif
+#ifndef MSCAN_FORCE_CHUNKS
+#define MSCAN_FORCE_CHUNKS 0
 #endif
 #ifndef MSCAN_MIN_CHUNK
 #define MSCAN_MIN_CHUNK 1024     // shortest time chunk worth a separate aggregate pass
@@ -35,13 +44,25 @@ int kinds_of(int mode) {
   }
 }
 
-// States per lane for a state size N (waves per workgroup = N / G).
-int states_per_lane(int64_t N) { return N <= 4 ? (int)N : N <= 16 ? 4 : (int)(N / 4); }
+// Workgroup layouts: CB channels per workgroup, G states per thread,
+// CB*N/G threads.  Layout 0 (64 channels, N/4 states per thread, 4 waves) is
+// the cheapest per element: the readout sums 4 partials per (token, channel)
+// and each wave's B, C reads are wave-uniform.  Layout 2 uses 16-channel
+// blocks with one state per thread (for N = 16) to spread few rows over
+// every CU, at a higher LDS cost per element.  State sizes below 16 use
+// layout 0 only.
+struct Layout {
+  int cb, g;
+};
+constexpr Layout layout_of(int N, int id) {
+  return N < 16 ? Layout{64, N < 4 ? N : 4} : id == 2 ? Layout{16, N / 16} : Layout{64, N / 4};
+}
+constexpr int threads_of(int N, int id) { return layout_of(N, id).cb * N / layout_of(N, id).g; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Plan {
-  int K, Ku, nblk_d, nchunks, chunk_len;
+  int K, Ku, layout, cb, nblk_d, nchunks, chunk_len;
   size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
   size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
 };
@@ -65,17 +86,45 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   if (g->seqlen > INT32_MAX / 2 || g->dim > INT32_MAX / 2 || g->batch > INT32_MAX / 8 ||
       g->batch * g->dim > INT32_MAX / 4)
     return MAMBA_ERR_UNSUPPORTED;
+  // each (batch, direction) slice of L x D elements is addressed through a
+  // buffer descriptor with 32-bit offsets (fp32 rows for several directions)
+  const int64_t es = g->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
+  if (g->seqlen * g->dim * es > INT32_MAX || (K > 1 && g->seqlen * g->dim * 4 > INT32_MAX))
+    return MAMBA_ERR_UNSUPPORTED;
   pl->K = K;
   pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
-  pl->nblk_d = (int)((g->dim + 63) / 64);
-  const int64_t nw = (int64_t)K * g->batch * pl->nblk_d * (N / states_per_lane(N));
+  // Layout and time split.  Waves wanted: MSCAN_TARGET_WAVES (3 per SIMD),
+  // since one wave alone issues vector instructions at about half the SIMD rate.
   const int64_t L = g->seqlen;
+  const int64_t rows64 = (int64_t)K * g->batch * ((g->dim + 63) / 64);
+  const int64_t waves0 = rows64 * (threads_of((int)N, 0) / 64);
+  int layout = 0;
   int64_t nch = 1;
-  if (nw < MSCAN_TARGET_WAVES && L >= 2 * MSCAN_MIN_CHUNK) {
-    nch = (MSCAN_TARGET_WAVES + nw - 1) / nw;
-    if (nch > L / MSCAN_MIN_CHUNK) nch = L / MSCAN_MIN_CHUNK;
-    if (nch > MSCAN_MAX_CHUNKS) nch = MSCAN_MAX_CHUNKS;
+  auto split = [&](int64_t waves) {
+    int64_t c = (MSCAN_TARGET_WAVES + waves - 1) / waves;
+    if (c > L / MSCAN_MIN_CHUNK) c = L / MSCAN_MIN_CHUNK;
+    if (c > MSCAN_MAX_CHUNKS) c = MSCAN_MAX_CHUNKS;
+    return c < 1 ? (int64_t)1 : c;
+  };
+  // Measured on MI355X: layout 0 is fastest whenever it yields at least 1.5
+  // waves per SIMD, and for long sequences split in time; short sequences with
+  // few rows are faster on 16-channel blocks than split in time.
+  if (waves0 < MSCAN_TARGET_WAVES / 2) {
+    if (N >= 16 && L < 8 * MSCAN_MIN_CHUNK) {
+      layout = 2;
+      const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
+      if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2);
+    } else if (L >= 2 * MSCAN_MIN_CHUNK) {
+      nch = split(waves0);
+    }
   }
+  if ((MSCAN_FORCE_LAYOUT == 0 || MSCAN_FORCE_LAYOUT == 2) && N >= 16) layout = MSCAN_FORCE_LAYOUT;
+  if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
+  if (nch < 1) nch = 1;
+  const int cb = layout_of((int)N, layout).cb;
+  pl->layout = layout;
+  pl->cb = cb;
+  pl->nblk_d = (int)((g->dim + cb - 1) / cb);
   int64_t clen = (L + nch - 1) / nch;
   clen = (clen + kTile - 1) / kTile * kTile;
   nch = (L + clen - 1) / clen;
@@ -90,21 +139,32 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   return MAMBA_OK;
 }
 
-template <typename TIn, int N>
-int launch_scan(const ScanParams& base, const Plan& pl, hipStream_t stream) {
-  constexpr int G = N <= 4 ? N : N <= 16 ? 4 : N / 4;
-  constexpr int NT = 64 * (N / G);
-  ScanParams p = base;
+template <typename TIn, int N, int LID>
+int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
+  constexpr Layout lay = layout_of(N, LID);
+  constexpr int NT = threads_of(N, LID);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, G, kTile, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true>), dim3(blocks), dim3(NT), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.grid_chunks = pl.nchunks;
   const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, G, kTile, false>), dim3(blocks), dim3(NT), 0, stream, p);
-  if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false>), dim3(blocks), dim3(NT), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TIn, int N>
+int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
+  int rc = MAMBA_ERR_UNSUPPORTED;
+  if constexpr (N >= 16) {
+    if (pl.layout == 2) rc = launch_chunks<TIn, N, 2>(p, pl, stream);
+    else rc = launch_chunks<TIn, N, 0>(p, pl, stream);
+  } else {
+    rc = launch_chunks<TIn, N, 0>(p, pl, stream);
+  }
+  if (rc != MAMBA_OK) return rc;
   if (p.ws_y) {
     const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
     const unsigned mblocks = (unsigned)((rows8 + 255) / 256);

@@ -75,27 +75,51 @@ struct ScanParams {
   int softplus;
 };
 
-template <typename TIn, int N, int G, int TT, bool AGG>
-__global__ void __launch_bounds__(64 * (N / G)) scan_chunk_kernel(const ScanParams p) {
-  constexpr int NW = N / G;
-  constexpr int NT = 64 * NW;
-  constexpr int SPT = (TT * 8) / NT;  // (token, 8-channel group) slots per thread per tile
-  static_assert(SPT * NT == TT * 8, "tile must split evenly into 8-channel slots");
-  constexpr int EQ = N < 4 ? N : 4;   // B/C elements per load unit
-  constexpr int UPR = N / EQ;         // load units per token row
-  constexpr int BCU = TT * UPR;       // load units per tile per tensor
-  constexpr int BCI = (BCU + NT - 1) / NT;
+// Maps blockIdx.x to the logical workgroup index so that the 64/CB workgroups
+// covering one 64-channel (128-byte bf16) row segment run on the same XCD:
+// consecutive blockIdx values go round-robin to the 8 XCDs, each with its own L2.
+__device__ __forceinline__ int logical_block(int bid, int nblocks, int S) {
+  if (S == 1) return bid;
+  const int span = 8 * S;
+  const int full = nblocks / span * span;
+  if (bid >= full) return bid;
+  const int j = (bid / span) * 8 + (bid % 8);  // group of S logical blocks
+  const int s = (bid / 8) % S;
+  return j * S + s;
+}
 
-  __shared__ float2 s_dd[TT][64];  // (Δ, Δ·u) per scan step and channel
+// One workgroup scans CB consecutive channels of one (direction k, batch b) over
+// one chunk of scan positions.  Thread i owns channel c = i % CB and the state
+// group ng = i / CB (states ng*G .. ng*G+G-1); NT = CB*N/G threads.  For the
+// staging and the epilogue the same thread owns channel c and the TPT = TT/NG
+// consecutive scan positions ng*TPT .. ng*TPT+TPT-1 of each tile.
+template <typename TIn, int N, int G, int CB, int TT, bool AGG>
+__global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams p) {
+  constexpr int NG = N / G;    // state groups per channel
+  constexpr int NT = CB * NG;  // threads per workgroup
+  static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
+  static_assert(TT % NG == 0, "tile splits evenly over state groups");
+  constexpr int TPT = TT / NG;            // tile positions staged per thread
+  constexpr int EQ = N < 4 ? N : 4;       // B/C elements per load unit
+  constexpr int UPR = N / EQ;             // load units per token row
+  constexpr int BCU = TT * UPR;           // load units per tile per tensor
+  constexpr int BCI = (BCU + NT - 1) / NT;
+  constexpr int YS = TT + 4;              // partial-readout row: stride 36 dwords, conflict-free b128
+  static_assert(TT % 4 == 0, "the scan loop runs 4 steps per iteration");
+
+  __shared__ float2 s_dd[TT][CB];  // (Δ'_t, Δ_t·u_t) per step and channel
   __shared__ float s_B[TT][N];
   __shared__ float s_C[AGG ? 1 : TT][N];
-  __shared__ float s_y[AGG ? 1 : NW][AGG ? 1 : TT][64];  // partial readouts per wave
+  __shared__ float s_y[AGG ? 1 : NG][AGG ? 1 : CB][AGG ? 4 : YS];  // partial readouts, time-contiguous
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
+  const int cl = tid % CB;  // channel within the block
+  // state group (scan) / position group (staging, epilogue); wave-uniform when
+  // a wave spans the whole 64-channel block, and then kept in a scalar register
+  const int ng = CB == 64 ? __builtin_amdgcn_readfirstlane(tid / CB) : tid / CB;
 
-  int bid = blockIdx.x;
+  const int nblocks = gridDim.x;
+  int bid = logical_block(blockIdx.x, nblocks, 64 / CB < 1 ? 1 : 64 / CB);
   const int dblk = bid % p.nblk_d;
   bid /= p.nblk_d;
   const int c = bid % p.grid_chunks;
@@ -104,205 +128,260 @@ __global__ void __launch_bounds__(64 * (N / G)) scan_chunk_kernel(const ScanPara
   const int k = bid / p.Bsz;
 
   const int D = p.Dm, L = p.L;
-  const int d0 = dblk * 64;
-  const int d = d0 + lane;
+  const int d0 = dblk * CB;
+  const int d = d0 + cl;
   const bool dvalid = d < D;
   const int kind = (p.kinds >> (2 * k)) & 3;
   const int ku = (p.Ku == 1) ? 0 : k;
   const int pbeg = c * p.chunk_len;
   const int pend = min(L, pbeg + p.chunk_len);
 
-  const TIn* __restrict__ u_base = static_cast<const TIn*>(p.u) + (int64_t)(b * p.Ku + ku) * L * D;
-  const TIn* __restrict__ dl_base = static_cast<const TIn*>(p.delta) + (int64_t)(b * p.K + k) * L * D;
-  const TIn* __restrict__ z_base = p.z ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : nullptr;
+  // u, Δraw, z, out and the per-direction fp32 rows are read and written through
+  // buffer descriptors over this (k, b) slice: a scalar row offset plus the
+  // lane's constant channel offset, no per-access vector address arithmetic.
+  constexpr uint32_t ES = sizeof(TIn);
+  const uint32_t slice = (uint32_t)((int64_t)L * D * ES);
+  const TIn* u_slice = static_cast<const TIn*>(p.u) + (int64_t)(b * p.Ku + ku) * L * D;
+  const TIn* dl_slice = static_cast<const TIn*>(p.delta) + (int64_t)(b * p.K + k) * L * D;
+  const auto rs_u = make_rsrc(u_slice, slice);
+  const auto rs_dl = make_rsrc(dl_slice, slice);
+  const auto rs_z = make_rsrc(p.z ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : nullptr, p.z ? slice : 0u);
+  const auto rs_out = p.ws_y ? make_rsrc(p.ws_y + ((int64_t)k * p.Bsz + b) * L * D, (uint32_t)((int64_t)L * D * 4))
+                             : make_rsrc(static_cast<TIn*>(p.out) + (int64_t)b * L * D, slice);
   const TIn* __restrict__ B_base = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* __restrict__ C_base = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
-  const bool gated = !AGG && (z_base != nullptr) && (p.ws_y == nullptr);
+  const bool gated = !AGG && (p.z != nullptr) && (p.ws_y == nullptr);
 
   // ---- per-lane constants and the starting state ----
   float Al2[G], h[G];
 #pragma unroll
   for (int j = 0; j < G; ++j) {
-    const int n = wave * G + j;
-    Al2[j] = dvalid ? p.A[((int64_t)k * D + d) * N + n] * kLog2e : 0.f;
+    const int n = ng * G + j;
+    Al2[j] = dvalid ? p.A[((int64_t)k * D + d) * N + n] : 0.f;  // 2^(Δ'·A) = e^(Δ·A)
     h[j] = 0.f;
   }
   const int64_t agg_row = ((int64_t)k * p.Bsz + b) * (p.nchunks - 1);
   if (c == 0) {
     if (p.init_state && dvalid) {
 #pragma unroll
-      for (int j = 0; j < G; ++j) h[j] = p.init_state[(((int64_t)b * p.K + k) * D + d) * N + wave * G + j];
+      for (int j = 0; j < G; ++j) h[j] = p.init_state[(((int64_t)b * p.K + k) * D + d) * N + ng * G + j];
     }
   } else if (!AGG && dvalid) {
-    // fold the aggregates of chunks 0..c-1: h <- exp(A·ΣΔ_j)·h + S_j
+    // fold the aggregates of chunks 0..c-1: h <- exp(A·ΣΔ_j)·h + S_j, ΣΔ_j kept as ΣΔ'_j
     for (int jj = 0; jj < c; ++jj) {
       const float ds = p.agg_dsum[(agg_row + jj) * D + d];
-      const float* S = p.agg_state + ((agg_row + jj) * D + d) * N + wave * G;
+      const float* S = p.agg_state + ((agg_row + jj) * D + d) * N + ng * G;
 #pragma unroll
       for (int j = 0; j < G; ++j) h[j] = __builtin_fmaf(ex2(ds * Al2[j]), h[j], S[j]);
     }
   }
-
+  const float bias = (dvalid && p.delta_bias) ? p.delta_bias[k * D + d] : 0.f;
+  const float Dd = (dvalid && p.D) ? p.D[k * D + d] : 0.f;
   // The state registers may still be waiting on the loads above; settle them
   // here so that no wait on global loads lands inside the scan loop, where it
   // would also wait for the next tile's prefetch.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- per-slot constants: channel group of this thread's slots is fixed ----
-  const int c8 = tid & 7;
-  const int dg = d0 + c8 * 8;
-  const bool gvalid = dg < D;
-  float bias8[8], D8[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    bias8[j] = (gvalid && p.delta_bias) ? p.delta_bias[k * D + dg + j] : 0.f;
-    D8[j] = (gvalid && p.D) ? p.D[k * D + dg + j] : 0.f;
-  }
+  // Row-major traversals (every direction except the cross scan's column-major
+  // ones) visit a tile's tokens as one contiguous run: token row offsets are
+  // then scalars and each access is a scalar base plus the lane's channel.
+  const bool rowwise = kind < KIND_COL_FWD;
+  const bool rev = kind == KIND_ROW_REV;
+  auto token = [&](int pp) { return rowwise ? (rev ? L - 1 - pp : pp) : token_of(kind, pp, L, p.H, p.W); };
 
-  Vec8<TIn> rdl[SPT], ru[SPT], rz[SPT];
-  Small<TIn, EQ> rB[BCI], rC[BCI];
-  float Du[SPT][8], gate[SPT][8];
+  // raw (undecoded) loads of one tile; two sets rotate so that a tile's loads
+  // are issued two tiles before it is staged
+  struct Raw {
+    TIn dl[TPT], u[TPT], z[TPT];
+    Small<TIn, EQ> B[BCI], C[BCI];
+  };
+  Raw r0, r1;
+  float Du[TPT], gate[TPT];
 #pragma unroll
-  for (int i = 0; i < SPT; ++i) {
-    rdl[i].zero();
-    ru[i].zero();
-    rz[i].zero();
+  for (int i = 0; i < TPT; ++i) {
+    r0.dl[i] = r0.u[i] = r0.z[i] = r1.dl[i] = r1.u[i] = r1.z[i] = TIn(0);
+    Du[i] = 0.f;
+    gate[i] = 1.f;
   }
 #pragma unroll
   for (int i = 0; i < BCI; ++i) {
-    rB[i].zero();
-    rC[i].zero();
+    r0.B[i].zero();
+    r0.C[i].zero();
+    r1.B[i].zero();
+    r1.C[i].zero();
   }
 
-  auto load_tile = [&](int p0) {
+  // Element offsets of this thread's channel; rows outside the chunk and
+  // channels beyond D are clamped to valid addresses (their values are zeroed
+  // at staging and never stored).
+  const int dlast = D - 1 - d0;
+  const uint32_t voff_in = (uint32_t)(d0 + min(cl, dlast)) * ES;
+  const uint32_t voff_out = (uint32_t)(d0 + min(cl, dlast)) * (p.ws_y ? 4u : ES);
+  const bool dfull = d0 + CB <= D;
+  auto row_elem = [&](int pp) { return (uint32_t)token(min(pp, pend - 1)) * (uint32_t)D; };
+  // Loads are issued unconditionally (rows clamped into the chunk), so the
+  // wait before staging covers exactly the older of the two tiles in flight.
+  auto load_tile = [&](int p0, Raw& r) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int tt = (tid + i * NT) >> 3;
-      const int pp = p0 + tt;
-      if (pp < pend && gvalid) {
-        const int64_t off = (int64_t)token_of(kind, pp, L, p.H, p.W) * D + dg;
-        rdl[i].load(dl_base + off);
-        ru[i].load(u_base + off);
-        if (gated) rz[i].load(z_base + off);
-      }
+    for (int i = 0; i < TPT; ++i) {
+      // the row offset is a scalar only when the wave's rows are one row (CB = 64)
+      const uint32_t roff = row_elem(p0 + ng * TPT + i) * ES;
+      const uint32_t soff = CB == 64 ? roff : 0u;
+      const uint32_t voff = CB == 64 ? voff_in : voff_in + roff;
+      r.dl[i] = buf_load(rs_dl, voff, soff, (TIn*)nullptr);
+      r.u[i] = buf_load(rs_u, voff, soff, (TIn*)nullptr);
+      if (gated) r.z[i] = buf_load(rs_z, voff, soff, (TIn*)nullptr);
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
-      const int q = tid + i * NT;
-      if (q < BCU) {
-        const int tt = q / UPR, nq = q % UPR;
-        const int pp = p0 + tt;
-        if (pp < pend) {
-          const int64_t off = (int64_t)token_of(kind, pp, L, p.H, p.W) * N + nq * EQ;
-          rB[i].load(B_base + off);
-          if constexpr (!AGG) rC[i].load(C_base + off);
-        }
-      }
+      const int q = min(tid + i * NT, BCU - 1);
+      const int tt = q / UPR, nq = q % UPR;
+      const int64_t off = (int64_t)token(min(p0 + tt, pend - 1)) * N + nq * EQ;
+      r.B[i].load(B_base + off);
+      if constexpr (!AGG) r.C[i].load(C_base + off);
     }
   };
 
-  auto stage_tile = [&](int p0) {
+  auto stage_tile = [&](int p0, const Raw& r) {
 #pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-      const int tt = (tid + i * NT) >> 3;
-      const bool ok = (p0 + tt < pend) && gvalid;
-      float2 dd[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // branch-free: compute on whatever the registers hold, then select
-        const float x = rdl[i].get(j) + bias8[j];
-        const float sp = softplus_f(x);
-        const float dl = ok ? (p.softplus ? sp : x) : 0.f;
-        const float uu = ok ? ru[i].get(j) : 0.f;
-        dd[j] = make_float2(dl, dl * uu);
-        if constexpr (!AGG) {
-          Du[i][j] = D8[j] * uu;
-          if (gated) gate[i][j] = silu_f(rz[i].get(j));
-        }
+    for (int i = 0; i < TPT; ++i) {
+      const int tt = ng * TPT + i;
+      const bool ok = (p0 + tt < pend) && dvalid;
+      // branch-free: compute on whatever the registers hold, then select
+      const float x = to_f32(r.dl[i]) + bias;
+      const float sp = softplus_log2(x);
+      const float dl = ok ? (p.softplus ? sp : x * kLog2e) : 0.f;  // Δ' = Δ·log2 e
+      const float uu = ok ? to_f32(r.u[i]) : 0.f;
+      s_dd[tt][cl] = make_float2(dl, dl * uu);
+      if constexpr (!AGG) {
+        Du[i] = Dd * uu;
+        if (gated) gate[i] = silu_f(to_f32(r.z[i]));
       }
-      float4* dst = reinterpret_cast<float4*>(&s_dd[tt][c8 * 8]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = make_float4(dd[2 * j].x, dd[2 * j].y, dd[2 * j + 1].x, dd[2 * j + 1].y);
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
       const int q = tid + i * NT;
       if (q < BCU) {
         const int tt = q / UPR, nq = q % UPR;
-        const bool ok = p0 + tt < pend;
+        const bool okq = p0 + tt < pend;
 #pragma unroll
         for (int e = 0; e < EQ; ++e) {
-          s_B[tt][nq * EQ + e] = ok ? rB[i].get(e) : 0.f;
-          if constexpr (!AGG) s_C[tt][nq * EQ + e] = ok ? rC[i].get(e) : 0.f;
+          s_B[tt][nq * EQ + e] = okq ? r.B[i].get(e) * kLn2 : 0.f;  // Δ·B = Δ'·(B·ln 2)
+          if constexpr (!AGG) s_C[tt][nq * EQ + e] = okq ? r.C[i].get(e) : 0.f;
         }
       }
     }
   };
 
   float dsum = 0.f;
-  if (pbeg < pend) {
-    load_tile(pbeg);
-    stage_tile(pbeg);
-  }
-  for (int p0 = pbeg; p0 < pend; p0 += TT) {
-    const bool has_next = p0 + TT < pend;
-    if (has_next) load_tile(p0 + TT);  // in flight during this tile's scan
+  // one tile: barrier, scan, barrier, epilogue (the next tile is staged by the caller)
+  auto process_tile = [&](int p0) {
     __syncthreads();
     const int tlen = min(TT, pend - p0);
-    for (int tt = 0; tt < tlen; ++tt) {
-      const float2 dd = s_dd[tt][lane];
-      float y = 0.f;
+    // Rows of the tile past the chunk end were staged as Δ' = 0, Δu = 0, B = C = 0:
+    // such a step leaves the state exactly unchanged (Ā = 2^0 = 1, input 0), so
+    // the loop runs branch-free over whole groups of 4 steps.  Software-pipelined
+    // over two register sets: the operands of the next two steps are read from
+    // LDS while the current two compute.
+    const int tend = (tlen + 3) & ~3;
+    struct Ops {
+      float2 dd[2];  // (Δ'_t, Δ_t·u_t) for two steps
+      float B[2][G], C[2][G];
+    };
+    auto read_ops = [&](Ops& o, int tt) {
+      o.dd[0] = s_dd[tt][cl];
+      o.dd[1] = s_dd[tt + 1][cl];
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          o.B[r][j] = s_B[tt + r][ng * G + j];
+          if constexpr (!AGG) o.C[r][j] = s_C[tt + r][ng * G + j];
+        }
+    };
+    // One pair of steps: every exp and input product first (they do not depend on
+    // the state), then the two dependent state updates and partial readouts.
+    auto pair = [&](const Ops& o, float& y0, float& y1) {
+      float a[2][G], bu[2][G];
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        const int n = wave * G + j;
-        const float a = ex2(dd.x * Al2[j]);
-        h[j] = __builtin_fmaf(a, h[j], dd.y * s_B[tt][n]);
-        if constexpr (!AGG) y = __builtin_fmaf(s_C[tt][n], h[j], y);
+        a[0][j] = ex2(o.dd[0].x * Al2[j]);
+        a[1][j] = ex2(o.dd[1].x * Al2[j]);
+        bu[0][j] = o.dd[0].y * o.B[0][j];
+        bu[1][j] = o.dd[1].y * o.B[1][j];
       }
-      if constexpr (!AGG) s_y[wave][tt][lane] = y;
-      if constexpr (AGG) dsum += dd.x;
+      float y[2] = {0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          h[j] = __builtin_fmaf(a[r][j], h[j], bu[r][j]);
+          if constexpr (!AGG) y[r] = __builtin_fmaf(o.C[r][j], h[j], y[r]);
+        }
+      }
+      y0 = y[0];
+      y1 = y[1];
+      if constexpr (AGG) dsum += o.dd[0].x + o.dd[1].x;
+    };
+    Ops o0, o1;
+    read_ops(o0, 0);
+    for (int tt = 0; tt < tend; tt += 4) {
+      float y[4];
+      read_ops(o1, tt + 2);
+      pair(o0, y[0], y[1]);
+      read_ops(o0, min(tt + 4, TT - 4));  // the last prefetch re-reads rows that go unused
+      pair(o1, y[2], y[3]);
+      if constexpr (!AGG) *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
     }
     __syncthreads();
     if constexpr (!AGG) {
+      // epilogue: this thread's channel at positions ng*TPT .. ng*TPT+TPT-1
+      float yv[TPT];
 #pragma unroll
-      for (int i = 0; i < SPT; ++i) {
-        const int tt = (tid + i * NT) >> 3;
-        const int pp = p0 + tt;
-        if (pp < pend && gvalid) {
-          float y8[8];
+      for (int i = 0; i < TPT; ++i) yv[i] = Du[i];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y8[j] = Du[i][j];
+      for (int g = 0; g < NG; ++g) {
 #pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            const float4 a = reinterpret_cast<const float4*>(&s_y[w][tt][c8 * 8])[0];
-            const float4 bq = reinterpret_cast<const float4*>(&s_y[w][tt][c8 * 8])[1];
-            y8[0] += a.x; y8[1] += a.y; y8[2] += a.z; y8[3] += a.w;
-            y8[4] += bq.x; y8[5] += bq.y; y8[6] += bq.z; y8[7] += bq.w;
-          }
-          const int64_t off = (int64_t)token_of(kind, pp, L, p.H, p.W) * D + dg;
-          if (p.ws_y) {
-            store8(p.ws_y + ((int64_t)k * p.Bsz + b) * L * D + off, y8);
-          } else {
-            if (gated) {
+        for (int i = 0; i < TPT; ++i) yv[i] += s_y[g][cl][ng * TPT + i];
+      }
+      const uint32_t oes = p.ws_y ? 4u : ES;
 #pragma unroll
-              for (int j = 0; j < 8; ++j) y8[j] *= gate[i][j];
-            }
-            store8(static_cast<TIn*>(p.out) + (int64_t)b * L * D + off, y8);
-          }
+      for (int i = 0; i < TPT; ++i) {
+        const int pp = p0 + ng * TPT + i;
+        if (pp < pend && (dfull || dvalid)) {
+          const uint32_t roff = row_elem(pp) * oes;
+          const uint32_t soff = CB == 64 ? roff : 0u;
+          const uint32_t voff = CB == 64 ? voff_out : voff_out + roff;
+          if (p.ws_y) buf_store(yv[i], rs_out, voff, soff);
+          else store_out(gated ? yv[i] * gate[i] : yv[i], rs_out, voff, soff, (TIn*)nullptr);
         }
       }
     }
-    if (has_next) stage_tile(p0 + TT);
+  };
+  if (pbeg < pend) {
+    load_tile(pbeg, r0);
+    load_tile(pbeg + TT, r1);
+    stage_tile(pbeg, r0);
+  }
+  for (int p0 = pbeg; p0 < pend; p0 += 2 * TT) {
+    load_tile(p0 + 2 * TT, r0);  // two tiles ahead
+    process_tile(p0);
+    if (p0 + TT < pend) {
+      stage_tile(p0 + TT, r1);
+      load_tile(p0 + 3 * TT, r1);
+      process_tile(p0 + TT);
+      if (p0 + 2 * TT < pend) stage_tile(p0 + 2 * TT, r0);
+    }
   }
 
   if (!dvalid) return;
   if constexpr (AGG) {
-    float* S = p.agg_state + ((agg_row + c) * D + d) * N + wave * G;
+    float* S = p.agg_state + ((agg_row + c) * D + d) * N + ng * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) S[j] = h[j];
-    if (wave == 0) p.agg_dsum[(agg_row + c) * D + d] = dsum;
+    if (ng == 0) p.agg_dsum[(agg_row + c) * D + d] = dsum;
   } else if (c == p.nchunks - 1 && p.last_state) {
-    float* S = p.last_state + (((int64_t)b * p.K + k) * D + d) * N + wave * G;
+    float* S = p.last_state + (((int64_t)b * p.K + k) * D + d) * N + ng * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) S[j] = h[j];
   }
@@ -331,12 +410,12 @@ __global__ void __launch_bounds__(256) merge_dirs_kernel(const float* __restrict
     y8[4] += bq.x; y8[5] += bq.y; y8[6] += bq.z; y8[7] += bq.w;
   }
   if (z) {
-    Vec8<TIn> zz;
+    Vec<TIn, 8> zz;
     zz.load(z + off);
 #pragma unroll
     for (int j = 0; j < 8; ++j) y8[j] *= silu_f(zz.get(j));
   }
-  store8(out + off, y8);
+  storeV<8>(out + off, y8);
 }
 
 // One recurrent step [MFS §2.3]: one thread per (b, d) holding all N states.
@@ -362,9 +441,9 @@ __global__ void __launch_bounds__(256) scan_step_kernel(const StepParams p) {
   const TIn* Bt = static_cast<const TIn*>(p.B_t) + (int64_t)b * N;
   const TIn* Ct = static_cast<const TIn*>(p.C_t) + (int64_t)b * N;
   const float x = load1(static_cast<const TIn*>(p.delta_t) + i) + (p.delta_bias ? p.delta_bias[d] : 0.f);
-  const float dl = p.softplus ? softplus_f(x) : x;
+  const float dl = p.softplus ? softplus_log2(x) : x * kLog2e;  // Δ' = Δ·log2 e
   const float uu = load1(static_cast<const TIn*>(p.u_t) + i);
-  const float du = dl * uu;
+  const float du = dl * uu * kLn2;  // Δ·u
   float* st = p.state + (int64_t)i * N;
   const float* Ad = p.A + (int64_t)d * N;
   float y = 0.f;
@@ -379,7 +458,7 @@ __global__ void __launch_bounds__(256) scan_step_kernel(const StepParams p) {
     Cs.load(Ct + n0);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const float a = ex2(dl * (Ad[n0 + e] * kLog2e));
+      const float a = ex2(dl * Ad[n0 + e]);  // e^(Δ·A) = 2^(Δ'·A)
       hs[e] = __builtin_fmaf(a, hv.get(e), du * Bs.get(e));
       y = __builtin_fmaf(Cs.get(e), hs[e], y);
     }
