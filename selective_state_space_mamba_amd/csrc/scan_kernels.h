@@ -7,9 +7,9 @@
 //   [VIM] "Vision Mamba：从状态空间模型到视觉革命的跨越" (x-humanoid.csdn.net)
 //
 // Work decomposition of scan_chunk_kernel (one workgroup):
-//   * 64 consecutive channels d of one (direction k, batch b), one lane per
-//     channel; the N states of a channel are split over NW = N/G waves, each
-//     lane holding G states h[n] in registers for the whole scan;
+//   * CB consecutive channels d of one (direction k, batch b); thread i owns
+//     channel i mod CB and G of the N states of that channel, held in
+//     registers for the whole scan (NG = N/G threads share a channel);
 //   * a contiguous range ("chunk") of scan positions; a sequence is split
 //     into several chunks only when (k, b, channel-block) rows alone cannot
 //     fill the GPU.  Chunks are joined by the associativity of the affine
@@ -18,21 +18,20 @@
 //     records its end state S_c and ΣΔ over the chunk (the chunk's decay is
 //     exp(A·ΣΔ) since Ā_t = exp(Δ_t·A)); the output pass folds the aggregates
 //     of the chunks before it into its starting state;
-//   * the chunk is streamed in tiles of TT scan positions: 128-bit coalesced
-//     loads of u, Δraw, z rows (each token's 64-channel row is contiguous in
-//     the token-major layout whatever the traversal order), prefetched one
-//     tile ahead into registers, then staged in LDS as (Δ, Δ·u) pairs (softplus
-//     and the Δ·u product computed once per (token, channel)) and fp32 B, C
-//     rows shared by every channel;
-//   * per scan step and state: Ā = 2^(Δ·A·log2 e) (one v_exp_f32),
-//     h = Ā·h + (Δu)·B, and the partial readout Σ C·h over the lane's G
-//     states [MFS §2.2 eq (2a)(2b); §6.2 Step 4 eq (4); MUN §4];
-//   * the NW partial readouts meet in LDS; the epilogue adds them in wave
-//     order, adds the D·u skip [MUN §4], applies the silu(z) gate [MFS §6.2
-//     Step 6] and stores 16-byte rows of the output.  With several
-//     directions the ungated fp32 row goes to a workspace slice instead and
-//     merge_dirs_kernel sums the directions in order and gates
-//     [VIM §2.2; S4M §3].
+//   * the chunk is streamed in tiles of TT scan positions: u, Δraw, z are
+//     read one element per thread per token through buffer descriptors (each
+//     token's channel row is contiguous in the token-major layout whatever the
+//     traversal order), two tiles ahead of use, then staged in LDS as
+//     (Δ', Δ'·u) pairs -- Δ' = Δ·log2 e, softplus and the product computed once
+//     per (token, channel) -- next to B·ln 2 and C rows shared by the channels;
+//   * per scan step and state: Ā = 2^(Δ'·A) = exp(Δ·A) (one v_exp_f32),
+//     h = Ā·h + (Δ'u)·(B ln 2), and the partial readout Σ C·h over the
+//     thread's G states [MFS §2.2 eq (2a)(2b); §6.2 Step 4 eq (4); MUN §4];
+//   * the NG partial readouts meet in LDS; the epilogue adds them in order,
+//     adds the D·u skip [MUN §4], applies the silu(z) gate [MFS §6.2 Step 6]
+//     and stores the output row.  With several directions the ungated fp32
+//     row goes to a workspace slice instead and merge_dirs_kernel sums the
+//     directions in order and gates [VIM §2.2; S4M §3].
 // No B·D·L·N intermediate is ever written to memory.
 #pragma once
 
