@@ -51,7 +51,7 @@ typedef enum {
   MAMBA_ERR_UNSUPPORTED = -2, /* valid but not built: N not a power of two in 1..64, dim not a
                                  multiple of 8, a pointer not 16-byte aligned, or sizes beyond
                                  the 32-bit offsets used inside one (batch, direction) slice:
-                                 seqlen*dim*sizeof(dtype) below 2^31 bytes, and for
+                                 (seqlen+64)*dim*sizeof(dtype) below 2^31 bytes, and for
                                  several directions seqlen*dim*4 below 2^31 bytes */
   MAMBA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mamba_scan_fwd_workspace_bytes() */
   MAMBA_ERR_HIP = -4          /* the HIP runtime rejected a launch */

@@ -122,6 +122,9 @@ __device__ __forceinline__ void storeV(float* p, const float (&y)[V]) {
   }
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // ---- E (1, 2 or 4) consecutive elements of B / C, kept as raw bits until used ----
 template <typename T, int E>
 struct Small;
@@ -131,6 +134,10 @@ struct Small<uint16_t, 4> {
   uint2 v;
   __device__ __forceinline__ void zero() { v = make_uint2(0, 0); }
   __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint2*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+    v = make_uint2(x[0], x[1]);
+  }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t w = e < 2 ? v.x : v.y;
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -157,6 +164,10 @@ struct Small<float, 4> {
   float4 v;
   __device__ __forceinline__ void zero() { v = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+    v = make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3]));
+  }
   __device__ __forceinline__ float get(int e) const { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 };
 template <>

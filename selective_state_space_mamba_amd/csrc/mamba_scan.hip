@@ -48,14 +48,14 @@ int kinds_of(int mode) {
 // CB*N/G threads.  Layout 0 (64 channels, N/4 states per thread, 4 waves) is
 // the cheapest per element: the readout sums 4 partials per (token, channel)
 // and each wave's B, C reads are wave-uniform.  Layout 2 uses 16-channel
-// blocks with one state per thread (for N = 16) to spread few rows over
-// every CU, at a higher LDS cost per element.  State sizes below 16 use
-// layout 0 only.
+// blocks with N/16 states per thread to spread few rows over every CU, at a
+// higher LDS cost per element.  State sizes below 16 use layout 0 only, state
+// sizes above 16 layout 2 only (at most 4 states per thread).
 struct Layout {
   int cb, g;
 };
 constexpr Layout layout_of(int N, int id) {
-  return N < 16 ? Layout{64, N < 4 ? N : 4} : id == 2 ? Layout{16, N / 16} : Layout{64, N / 4};
+  return N < 16 ? Layout{64, N < 4 ? N : 4} : (id == 2 || N > 16) ? Layout{16, N / 16} : Layout{64, N / 4};
 }
 constexpr int threads_of(int N, int id) { return layout_of(N, id).cb * N / layout_of(N, id).g; }
 
@@ -89,7 +89,9 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   // each (batch, direction) slice of L x D elements is addressed through a
   // buffer descriptor with 32-bit offsets (fp32 rows for several directions)
   const int64_t es = g->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
-  if (g->seqlen * g->dim * es > INT32_MAX || (K > 1 && g->seqlen * g->dim * 4 > INT32_MAX))
+  // (64 rows of margin: prefetches past either end of the sequence must still
+  // map to offsets outside the slice without wrapping)
+  if ((g->seqlen + 64) * g->dim * es > INT32_MAX || (K > 1 && g->seqlen * g->dim * 4 > INT32_MAX))
     return MAMBA_ERR_UNSUPPORTED;
   pl->K = K;
   pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
@@ -109,7 +111,11 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   // Measured on MI355X: layout 0 is fastest whenever it yields at least 1.5
   // waves per SIMD, and for long sequences split in time; short sequences with
   // few rows are faster on 16-channel blocks than split in time.
-  if (waves0 < MSCAN_TARGET_WAVES / 2) {
+  if (N > 16) {
+    layout = 2;
+    const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
+    if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2);
+  } else if (waves0 < MSCAN_TARGET_WAVES / 2) {
     if (N >= 16 && L < 8 * MSCAN_MIN_CHUNK) {
       layout = 2;
       const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
@@ -118,7 +124,7 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
       nch = split(waves0);
     }
   }
-  if ((MSCAN_FORCE_LAYOUT == 0 || MSCAN_FORCE_LAYOUT == 2) && N >= 16) layout = MSCAN_FORCE_LAYOUT;
+  if ((MSCAN_FORCE_LAYOUT == 0 || MSCAN_FORCE_LAYOUT == 2) && N == 16) layout = MSCAN_FORCE_LAYOUT;
   if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
   if (nch < 1) nch = 1;
   const int cb = layout_of((int)N, layout).cb;
@@ -158,7 +164,9 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
 template <typename TIn, int N>
 int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
   int rc = MAMBA_ERR_UNSUPPORTED;
-  if constexpr (N >= 16) {
+  if constexpr (N > 16) {
+    rc = launch_chunks<TIn, N, 2>(p, pl, stream);
+  } else if constexpr (N == 16) {
     if (pl.layout == 2) rc = launch_chunks<TIn, N, 2>(p, pl, stream);
     else rc = launch_chunks<TIn, N, 0>(p, pl, stream);
   } else {

@@ -104,11 +104,16 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   constexpr int BCU = TT * UPR;           // load units per tile per tensor
   constexpr int BCI = (BCU + NT - 1) / NT;
   constexpr int YS = TT + 4;              // partial-readout row: stride 36 dwords, conflict-free b128
-  static_assert(TT % 4 == 0, "the scan loop runs 4 steps per iteration");
+  constexpr int DS = 2 * TT + 4;          // (Δ', Δu) row of one channel: 68 dwords, conflict-free b128
+  constexpr int BS = TT + 4;              // B or C row of one state: 36 dwords
+  static_assert(TT % 4 == 0 && TPT % 2 == 0, "the scan loop runs 4 steps per iteration");
+  static_assert(G <= 4, "at most 4 states per thread");
 
-  __shared__ float2 s_dd[TT][CB];  // (Δ'_t, Δ_t·u_t) per step and channel
-  __shared__ float s_B[TT][N];
-  __shared__ float s_C[AGG ? 1 : TT][N];
+  // Every LDS row is time-contiguous, so one 16-byte read serves 2 steps of
+  // (Δ', Δu) or 4 steps of B or C.
+  __shared__ float s_dd[CB * DS];              // [c][2t] = Δ'_t, [c][2t+1] = Δ_t·u_t
+  __shared__ float s_B[N * BS];                // [n][t] = B_t[n]·ln 2
+  __shared__ float s_C[AGG ? 4 : N * BS];      // [n][t] = C_t[n]
   __shared__ float s_y[AGG ? 1 : NG][AGG ? 1 : CB][AGG ? 4 : YS];  // partial readouts, time-contiguous
 
   const int tid = threadIdx.x;
@@ -242,6 +247,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   };
 
   auto stage_tile = [&](int p0, const Raw& r) {
+    float dd[2 * TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int tt = ng * TPT + i;
@@ -251,12 +257,17 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       const float sp = softplus_log2(x);
       const float dl = ok ? (p.softplus ? sp : x * kLog2e) : 0.f;  // Δ' = Δ·log2 e
       const float uu = ok ? to_f32(r.u[i]) : 0.f;
-      s_dd[tt][cl] = make_float2(dl, dl * uu);
+      dd[2 * i] = dl;
+      dd[2 * i + 1] = dl * uu;
       if constexpr (!AGG) {
         Du[i] = Dd * uu;
         if (gated) gate[i] = silu_f(to_f32(r.z[i]));
       }
     }
+#pragma unroll
+    for (int m = 0; m < TPT / 2; ++m)
+      *reinterpret_cast<float4*>(&s_dd[cl * DS + 2 * ng * TPT + 4 * m]) =
+          make_float4(dd[4 * m], dd[4 * m + 1], dd[4 * m + 2], dd[4 * m + 3]);
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
       const int q = tid + i * NT;
@@ -265,8 +276,8 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         const bool okq = p0 + tt < pend;
 #pragma unroll
         for (int e = 0; e < EQ; ++e) {
-          s_B[tt][nq * EQ + e] = okq ? r.B[i].get(e) * kLn2 : 0.f;  // Δ·B = Δ'·(B·ln 2)
-          if constexpr (!AGG) s_C[tt][nq * EQ + e] = okq ? r.C[i].get(e) : 0.f;
+          s_B[(nq * EQ + e) * BS + tt] = okq ? r.B[i].get(e) * kLn2 : 0.f;  // Δ·B = Δ'·(B·ln 2)
+          if constexpr (!AGG) s_C[(nq * EQ + e) * BS + tt] = okq ? r.C[i].get(e) : 0.f;
         }
       }
     }
@@ -283,54 +294,62 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     // over two register sets: the operands of the next two steps are read from
     // LDS while the current two compute.
     const int tend = (tlen + 3) & ~3;
+    // Operands of 4 steps: two 16-byte reads of (Δ', Δu) and one of B and of C
+    // per state.  Software-pipelined over two sets: the next 4 steps' operands
+    // are read while the current 4 compute.
     struct Ops {
-      float2 dd[2];  // (Δ'_t, Δ_t·u_t) for two steps
-      float B[2][G], C[2][G];
+      float dl[4], du[4];
+      float B[G][4], C[G][4];
     };
     auto read_ops = [&](Ops& o, int tt) {
-      o.dd[0] = s_dd[tt][cl];
-      o.dd[1] = s_dd[tt + 1][cl];
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-          o.B[r][j] = s_B[tt + r][ng * G + j];
-          if constexpr (!AGG) o.C[r][j] = s_C[tt + r][ng * G + j];
-        }
-    };
-    // One pair of steps: every exp and input product first (they do not depend on
-    // the state), then the two dependent state updates and partial readouts.
-    auto pair = [&](const Ops& o, float& y0, float& y1) {
-      float a[2][G], bu[2][G];
+      const float4 d01 = *reinterpret_cast<const float4*>(&s_dd[cl * DS + 2 * tt]);
+      const float4 d23 = *reinterpret_cast<const float4*>(&s_dd[cl * DS + 2 * tt + 4]);
+      o.dl[0] = d01.x; o.du[0] = d01.y; o.dl[1] = d01.z; o.du[1] = d01.w;
+      o.dl[2] = d23.x; o.du[2] = d23.y; o.dl[3] = d23.z; o.du[3] = d23.w;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
-        a[0][j] = ex2(o.dd[0].x * Al2[j]);
-        a[1][j] = ex2(o.dd[1].x * Al2[j]);
-        bu[0][j] = o.dd[0].y * o.B[0][j];
-        bu[1][j] = o.dd[1].y * o.B[1][j];
+        const float4 bv = *reinterpret_cast<const float4*>(&s_B[(ng * G + j) * BS + tt]);
+        o.B[j][0] = bv.x; o.B[j][1] = bv.y; o.B[j][2] = bv.z; o.B[j][3] = bv.w;
+        if constexpr (!AGG) {
+          const float4 cv = *reinterpret_cast<const float4*>(&s_C[(ng * G + j) * BS + tt]);
+          o.C[j][0] = cv.x; o.C[j][1] = cv.y; o.C[j][2] = cv.z; o.C[j][3] = cv.w;
+        }
       }
-      float y[2] = {0.f, 0.f};
+    };
+    // Four steps: the exps and input products do not depend on the state; the
+    // state updates and partial readouts follow in step order.
+    auto quad = [&](const Ops& o, int tt) {
+      float a[4][G], bu[4][G];
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+          a[r][j] = ex2(o.dl[r] * Al2[j]);
+          bu[r][j] = o.du[r] * o.B[j][r];
+        }
+      float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
           h[j] = __builtin_fmaf(a[r][j], h[j], bu[r][j]);
-          if constexpr (!AGG) y[r] = __builtin_fmaf(o.C[r][j], h[j], y[r]);
+          if constexpr (!AGG) y[r] = __builtin_fmaf(o.C[j][r], h[j], y[r]);
         }
-      }
-      y0 = y[0];
-      y1 = y[1];
-      if constexpr (AGG) dsum += o.dd[0].x + o.dd[1].x;
+      if constexpr (AGG) dsum += (o.dl[0] + o.dl[1]) + (o.dl[2] + o.dl[3]);
+      else *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
     };
     Ops o0, o1;
     read_ops(o0, 0);
-    for (int tt = 0; tt < tend; tt += 4) {
-      float y[4];
-      read_ops(o1, tt + 2);
-      pair(o0, y[0], y[1]);
-      read_ops(o0, min(tt + 4, TT - 4));  // the last prefetch re-reads rows that go unused
-      pair(o1, y[2], y[3]);
-      if constexpr (!AGG) *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
+#pragma unroll
+    for (int tt = 0; tt < TT; tt += 8) {
+      if (tt < tend) {
+        read_ops(o1, tt + 4);
+        quad(o0, tt);
+        if (tt + 4 < tend) {
+          read_ops(o0, min(tt + 8, TT - 4));  // the last prefetch re-reads rows that go unused
+          quad(o1, tt + 4);
+        }
+      }
     }
     __syncthreads();
     if constexpr (!AGG) {

@@ -78,6 +78,11 @@ def test_fwd_validation(lib):
     assert call_fwd(lib, dims(seqlen=96, height=8, width=11), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
     assert call_fwd(lib, dims(seqlen=96), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
     assert call_fwd(lib, dims(dstate=12)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    # 32-bit slice offsets: (seqlen + 64) * dim * sizeof(dtype) must stay below 2^31 bytes
+    dim = 1 << 16
+    lmax = (2**31 - 1) // (dim * 2) - 64
+    assert ms.workspace_bytes(dims(batch=1, dim=dim, seqlen=lmax), ms.DIR_FWD) >= 0
+    assert call_fwd(lib, dims(batch=1, dim=dim, seqlen=lmax + 1)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(dstate=128)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(dim=60)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(), u=FAKE + 4) == ms._binding.MAMBA_ERR_UNSUPPORTED
