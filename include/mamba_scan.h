@@ -17,6 +17,7 @@
  *   Δ     = softplus(delta[t] + delta_bias[d])      [MFS §4.1 Algorithm 2; MUN §4]
  *   Ā_n   = exp(Δ·A[d][n])                          [MFS §6.2 Step 4, eq (4)]
  *   h[n]  = Ā_n·h[n] + Δ·B[t][n]·u[t]               [MFS §2.2 eq (2a); MUN §4: B̄ ≈ ΔB]
+ *           (exact_zoh: ((Ā_n - 1)/A[d][n])·B[t][n]·u[t] [MFS §6.2 eq (4)])
  *   y_k   = Σ_n C[t][n]·h[n] + D[d]·u[t]            [MFS eq (2b); MUN §4: y = Ch + Dx]
  * and the output is out[t] = (Σ_k y_k[t])·silu(z[t]) [MFS §6.2 Step 6; VIM §2.2].
  *
@@ -87,6 +88,9 @@ typedef struct {
   int64_t width;   /* MAMBA_DIR_CROSS2D only: grid columns W; else 0 */
   int32_t dtype;          /* mamba_dtype */
   int32_t delta_softplus; /* 1: Δ = softplus(delta + bias); 0: Δ = delta + bias */
+  int32_t exact_zoh;      /* 0: input term Δ·B·u (the simplified rule [MUN §4]);
+                             1: exact zero-order hold ((e^{ΔA} - 1)/A)·B·u, Δ·B·u where
+                             A = 0 [MFS §6.2 Step 4, eq (4)] */
   const float* initial_state; /* optional device pointer, [B][K][D][N] float32: state before
                                  each direction's first token; NULL = zeros */
   void* workspace;            /* device scratch owned by the caller (may be NULL when

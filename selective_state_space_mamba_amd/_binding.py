@@ -23,7 +23,7 @@ class MambaDims(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
         ("dstate", ctypes.c_int64), ("height", ctypes.c_int64), ("width", ctypes.c_int64),
-        ("dtype", ctypes.c_int32), ("delta_softplus", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("delta_softplus", ctypes.c_int32), ("exact_zoh", ctypes.c_int32),
         ("initial_state", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
     ]
@@ -94,10 +94,11 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-def make_dims(batch, dim, seqlen, dstate, dtype, *, height=0, width=0, delta_softplus=True,
+def make_dims(batch, dim, seqlen, dstate, dtype, *, height=0, width=0, delta_softplus=True, exact_zoh=False,
               initial_state=None, workspace=None, workspace_bytes=0) -> MambaDims:
     return MambaDims(int(batch), int(dim), int(seqlen), int(dstate), int(height), int(width), int(dtype),
-                     1 if delta_softplus else 0, _ptr(initial_state), _ptr(workspace), int(workspace_bytes))
+                     1 if delta_softplus else 0, 1 if exact_zoh else 0, _ptr(initial_state), _ptr(workspace),
+                     int(workspace_bytes))
 
 
 def workspace_bytes(dims: MambaDims, dir_mode: int) -> int:
@@ -121,8 +122,8 @@ def _check(t, name, shape, dtype, device):
 
 
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0, width=0,
-             delta_softplus=True, initial_state=None, out=None, last_state=None, want_last_state=True,
-             workspace=None, stream=None):
+             delta_softplus=True, exact_zoh=False, initial_state=None, out=None, last_state=None,
+             want_last_state=True, workspace=None, stream=None):
     """mamba_scan_fwd on torch tensors.
 
     Shapes (K directions; the K axis is absent when K = 1; u has no K axis for
@@ -155,7 +156,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
         last_state = torch.empty((Bsz,) + kx + (Dm, N), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
     dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
-                     initial_state=initial_state)
+                     exact_zoh=exact_zoh, initial_state=initial_state)
     need = workspace_bytes(dims, dir_mode)
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -170,7 +171,7 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
 
 
 def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None, *, delta_softplus=True,
-              out=None, stream=None):
+              exact_zoh=False, out=None, stream=None):
     """mamba_scan_step on torch tensors: state [B][D][N] float32 (updated in
     place), u_t/delta_t/z_t [B][D], B_t/C_t [B][N], A [D][N], D/delta_bias [D].
     Returns out [B][D]."""
@@ -191,7 +192,7 @@ def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=Non
     if out is None:
         out = torch.empty((Bsz, Dm), dtype=tdt, device=dev)
     _check(out, "out", (Bsz, Dm), tdt, dev)
-    dims = make_dims(Bsz, Dm, 1, N, dt, delta_softplus=delta_softplus)
+    dims = make_dims(Bsz, Dm, 1, N, dt, delta_softplus=delta_softplus, exact_zoh=exact_zoh)
     rc = lib.mamba_scan_step(_ptr(state), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D),
                              _ptr(z_t), _ptr(delta_bias), ctypes.byref(dims), _ptr(out), _stream(stream))
     if rc != MAMBA_OK:

@@ -30,6 +30,19 @@ __device__ __forceinline__ float softplus_log2(float x) {
   return __builtin_fmaxf(t, lg2(1.0f + ex2(__builtin_fminf(t, 64.0f))));
 }
 
+// Exact zero-order hold of the input term: B̄u = ((e^{ΔA} - 1)/A)·B·u = Δ·φ(ΔA)·B·u
+// with φ(x) = (e^x - 1)/x (φ(0) = 1, the A = 0 limit).  From the decay a = e^x
+// already computed, (a - 1)·(1/A) is accurate while |x| is not small; below
+// |x| = 1/16 the subtraction would cancel, and φ comes from its Taylor series
+// 1 + x/2 + x²/6 + x³/24 + x⁴/120, whose remainder there is below 2^-30.
+// Arguments: a = e^x, x = ΔA, dt = Δ, inv_a = 1/A (any value when A = 0).
+__device__ __forceinline__ float zoh_coef(float a, float x, float dt, float inv_a) {
+  const float direct = __builtin_fmaf(a, inv_a, -inv_a);
+  const float series =
+      __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f), 1.0f / 6.0f), 0.5f), 1.0f);
+  return __builtin_fabsf(x) < 0.0625f ? dt * series : direct;
+}
+
 // silu(z) = z·sigmoid(z) = z / (1 + e^{-z}); for z -> -inf, e^{-z} -> inf and
 // the reciprocal gives 0.
 __device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }

@@ -145,32 +145,32 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   return MAMBA_OK;
 }
 
-template <typename TIn, int N, int LID>
+template <typename TIn, int N, int LID, bool EXACT>
 int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
   constexpr Layout lay = layout_of(N, LID);
   constexpr int NT = threads_of(N, LID);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.grid_chunks = pl.nchunks;
   const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false>), dim3(blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
-template <typename TIn, int N>
+template <typename TIn, int N, bool EXACT>
 int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
   int rc = MAMBA_ERR_UNSUPPORTED;
   if constexpr (N > 16) {
-    rc = launch_chunks<TIn, N, 2>(p, pl, stream);
+    rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
   } else if constexpr (N == 16) {
-    if (pl.layout == 2) rc = launch_chunks<TIn, N, 2>(p, pl, stream);
-    else rc = launch_chunks<TIn, N, 0>(p, pl, stream);
+    if (pl.layout == 2) rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
+    else rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
   } else {
-    rc = launch_chunks<TIn, N, 0>(p, pl, stream);
+    rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
   }
   if (rc != MAMBA_OK) return rc;
   if (p.ws_y) {
@@ -184,37 +184,37 @@ int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
   return MAMBA_OK;
 }
 
-template <typename TIn>
+template <typename TIn, bool EXACT>
 int dispatch_scan(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s) {
   switch (N) {
-    case 1: return launch_scan<TIn, 1>(p, pl, s);
-    case 2: return launch_scan<TIn, 2>(p, pl, s);
-    case 4: return launch_scan<TIn, 4>(p, pl, s);
-    case 8: return launch_scan<TIn, 8>(p, pl, s);
-    case 16: return launch_scan<TIn, 16>(p, pl, s);
-    case 32: return launch_scan<TIn, 32>(p, pl, s);
-    case 64: return launch_scan<TIn, 64>(p, pl, s);
+    case 1: return launch_scan<TIn, 1, EXACT>(p, pl, s);
+    case 2: return launch_scan<TIn, 2, EXACT>(p, pl, s);
+    case 4: return launch_scan<TIn, 4, EXACT>(p, pl, s);
+    case 8: return launch_scan<TIn, 8, EXACT>(p, pl, s);
+    case 16: return launch_scan<TIn, 16, EXACT>(p, pl, s);
+    case 32: return launch_scan<TIn, 32, EXACT>(p, pl, s);
+    case 64: return launch_scan<TIn, 64, EXACT>(p, pl, s);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }
 
-template <typename TIn, int N>
+template <typename TIn, int N, bool EXACT>
 int launch_step(const StepParams& p, hipStream_t stream) {
   const unsigned blocks = (unsigned)((p.Bsz * p.Dm + 255) / 256);
-  hipLaunchKernelGGL((scan_step_kernel<TIn, N>), dim3(blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((scan_step_kernel<TIn, N, EXACT>), dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
-template <typename TIn>
+template <typename TIn, bool EXACT>
 int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
   switch (N) {
-    case 1: return launch_step<TIn, 1>(p, s);
-    case 2: return launch_step<TIn, 2>(p, s);
-    case 4: return launch_step<TIn, 4>(p, s);
-    case 8: return launch_step<TIn, 8>(p, s);
-    case 16: return launch_step<TIn, 16>(p, s);
-    case 32: return launch_step<TIn, 32>(p, s);
-    case 64: return launch_step<TIn, 64>(p, s);
+    case 1: return launch_step<TIn, 1, EXACT>(p, s);
+    case 2: return launch_step<TIn, 2, EXACT>(p, s);
+    case 4: return launch_step<TIn, 4, EXACT>(p, s);
+    case 8: return launch_step<TIn, 8, EXACT>(p, s);
+    case 16: return launch_step<TIn, 16, EXACT>(p, s);
+    case 32: return launch_step<TIn, 32, EXACT>(p, s);
+    case 64: return launch_step<TIn, 64, EXACT>(p, s);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }
@@ -271,8 +271,12 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
   p.chunk_len = pl.chunk_len;
   p.nblk_d = pl.nblk_d;
   p.softplus = dims->delta_softplus ? 1 : 0;
-  if (dims->dtype == MAMBA_DTYPE_BF16) return dispatch_scan<uint16_t>(dims->dstate, p, pl, stream);
-  return dispatch_scan<float>(dims->dstate, p, pl, stream);
+  const bool exact = dims->exact_zoh != 0;
+  if (dims->dtype == MAMBA_DTYPE_BF16)
+    return exact ? dispatch_scan<uint16_t, true>(dims->dstate, p, pl, stream)
+                 : dispatch_scan<uint16_t, false>(dims->dstate, p, pl, stream);
+  return exact ? dispatch_scan<float, true>(dims->dstate, p, pl, stream)
+               : dispatch_scan<float, false>(dims->dstate, p, pl, stream);
 }
 
 int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A, const void* B_t,
@@ -289,8 +293,10 @@ int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const fl
     if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
   StepParams p{state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, out,
                (int)dims->batch, (int)dims->dim, dims->delta_softplus ? 1 : 0};
-  if (dims->dtype == MAMBA_DTYPE_BF16) return dispatch_step<uint16_t>(N, p, stream);
-  return dispatch_step<float>(N, p, stream);
+  const bool exact = dims->exact_zoh != 0;
+  if (dims->dtype == MAMBA_DTYPE_BF16)
+    return exact ? dispatch_step<uint16_t, true>(N, p, stream) : dispatch_step<uint16_t, false>(N, p, stream);
+  return exact ? dispatch_step<float, true>(N, p, stream) : dispatch_step<float, false>(N, p, stream);
 }
 
 const char* mamba_status_string(int status) {

@@ -40,7 +40,7 @@ def run_and_check(w, x=None, name=None, **kw):
     x = x if x is not None else I.make_inputs(w)
     announce("%s %s" % (name or w.name, w))
     out, st = gpu_fwd(w, dev_inputs(x), **kw)
-    ref_out, ref_st = oracle_fwd(w, x, **{k: v for k, v in kw.items() if k in ("delta_softplus",)},
+    ref_out, ref_st = oracle_fwd(w, x, **{k: v for k, v in kw.items() if k in ("delta_softplus", "exact_zoh")},
                                  initial_state=(None if kw.get("initial_state") is None
                                                 else kw["initial_state"].cpu().numpy()))
     assert_close((name or w.name) + " out", from_dev(out), ref_out, w.dtype)
@@ -242,22 +242,22 @@ def test_cross_scan_transpose_symmetry():
 # ---------------------------------------------------------------------------------------------
 # decode step
 
-def run_decode(w, L0, steps, rows=None):
+def run_decode(w, L0, steps, rows=None, exact_zoh=False):
     x = I.make_inputs(w, seqlen=L0 + steps)
     head = {k: (v[:, :L0] if k in ("u", "delta", "B", "C", "z") else v) for k, v in x.items()}
     xd = dev_inputs({k: (np.ascontiguousarray(v) if v is not None else None) for k, v in head.items()})
     announce("decode %s L0=%d steps=%d" % (w.name, L0, steps))
-    _, st = gpu_fwd(w.with_(seqlen=L0), xd)
+    _, st = gpu_fwd(w.with_(seqlen=L0), xd, exact_zoh=exact_zoh)
     state = st.contiguous()
     # step-major copies so that each step's [B][D] / [B][N] slice is contiguous
     tail = {k: to_dev(np.ascontiguousarray(x[k][:, L0:].swapaxes(0, 1))) for k in ("u", "delta", "B", "C", "z")}
     outs = []
     for s in range(steps):
         outs.append(ms.scan_step(state, tail["u"][s], tail["delta"][s], xd["A"], tail["B"][s],
-                                 tail["C"][s], xd["D"], tail["z"][s], xd["delta_bias"]))
+                                 tail["C"][s], xd["D"], tail["z"][s], xd["delta_bias"], exact_zoh=exact_zoh))
     torch().cuda.synchronize()
     got = np.stack([from_dev(o) for o in outs], axis=1)  # [B][steps][D]
-    ref_out, ref_st = oracle_fwd(w.with_(seqlen=L0 + steps), x, rows=rows)
+    ref_out, ref_st = oracle_fwd(w.with_(seqlen=L0 + steps), x, rows=rows, exact_zoh=exact_zoh)
     return got, from_dev(state), ref_out, ref_st
 
 
@@ -270,6 +270,69 @@ def test_decode_continues_scan_small():
     got, st, ref_out, ref_st = run_decode(wf, 64, 16)
     assert_close("decode f32 out", got, ref_out[:, 64:], "f32")
     assert_close("decode f32 state", st, ref_st[:, 0], "f32")
+
+
+def test_decode_exact_zoh():
+    w = I.Workload("dec_exact", 2, 64, 0, 16, I.DIR_FWD, "f32", True, 53)
+    got, st, ref_out, ref_st = run_decode(w, 80, 24, exact_zoh=True)
+    assert_close("decode exact out", got, ref_out[:, 80:], "f32")
+    assert_close("decode exact state", st, ref_st[:, 0], "f32")
+
+
+# ---------------------------------------------------------------------------------------------
+# exact zero-order hold of the input term
+
+EXACT = {
+    "exact_fwd_f32": I.Workload("exact_fwd_f32", 2, 136, 300, 16, I.DIR_FWD, "f32", True, 61),
+    "exact_fwd_bf16": I.Workload("exact_fwd_bf16", 2, 72, 133, 16, I.DIR_FWD, "bf16", True, 62),
+    "exact_bidir_bf16": I.Workload("exact_bidir_bf16", 2, 72, 197, 16, I.DIR_BIDIR, "bf16", True, 63),
+    "exact_cross2d_f32": I.Workload("exact_cross2d_f32", 1, 16, 35, 8, I.DIR_CROSS2D, "f32", True, 64, 5, 7),
+    "exact_split_f32": I.Workload("exact_split_f32", 1, 72, 5000, 16, I.DIR_FWD, "f32", True, 65),
+    "exact_rows768_bf16": I.Workload("exact_rows768_bf16", 12, 1024, 70, 16, I.DIR_FWD, "bf16", True, 66),
+    "exact_N4_f32": I.Workload("exact_N4_f32", 2, 80, 70, 4, I.DIR_FWD, "f32", True, 67),
+    "exact_N64_f32": I.Workload("exact_N64_f32", 1, 64, 50, 64, I.DIR_FWD, "f32", True, 68),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXACT))
+def test_exact_zoh(name):
+    run_and_check(EXACT[name], exact_zoh=True)
+
+
+def test_exact_zoh_small_and_zero_decay():
+    """A spread over zero, tiny and large magnitudes, so that both the series
+    and the direct branch of (e^{ΔA} - 1)/A and the A = 0 limit are taken."""
+    w = I.Workload("exact_mixed_A", 2, 64, 120, 16, I.DIR_FWD, "f32", True, 69)
+    x = I.make_inputs(w)
+    r = np.random.Generator(np.random.PCG64(70))
+    A = -np.exp(r.uniform(np.log(1e-4), np.log(30.0), size=x["A"].shape)).astype(np.float32)
+    A[:, ::5] = 0.0  # every fifth state does not decay
+    x["A"] = A
+    run_and_check(w, x, name="exact_mixed_A", exact_zoh=True)
+    run_and_check(w, x, name="simplified_mixed_A")
+
+
+def test_exact_zoh_is_the_gated_rnn():
+    """One state, A = -1, B = C = 1, no skip, no gate: with exact hold the scan is
+    h_t = (1 - g_t) h_{t-1} + g_t u_t with g_t = sigmoid(delta_t + bias), computed
+    here directly in float64 (independent of the oracle)."""
+    w = I.Workload("gated_rnn", 2, 64, 257, 1, I.DIR_FWD, "f32", False, 71)
+    x = I.make_inputs(w)
+    x["A"] = np.full_like(x["A"], -1.0)
+    x["B"] = np.ones_like(x["B"])
+    x["C"] = np.ones_like(x["C"])
+    x["D"] = None
+    announce("gated rnn")
+    out, _ = gpu_fwd(w, dev_inputs(x), exact_zoh=True)
+    s = x["delta"].astype(np.float64) + x["delta_bias"].astype(np.float64)[None, None, :]
+    g = 1.0 / (1.0 + np.exp(-s))
+    u = x["u"].astype(np.float64)
+    h = np.zeros((w.batch, w.dim))
+    want = np.empty_like(u)
+    for t in range(w.seqlen):
+        h = (1.0 - g[:, t]) * h + g[:, t] * u[:, t]
+        want[:, t] = h
+    assert_close("gated rnn", from_dev(out), want, "f32")
 
 
 # ---------------------------------------------------------------------------------------------
