@@ -57,6 +57,8 @@ def source_hash() -> str:
     counter summary stays valid across comment-only edits."""
     h = hashlib.sha256()
     for f in ("include/mamba_scan.h", "selective_state_space_mamba_amd/csrc/mamba_scan.hip",
+              "selective_state_space_mamba_amd/csrc/scan_inst.hip",
+              "selective_state_space_mamba_amd/csrc/scan_launch.h",
               "selective_state_space_mamba_amd/csrc/scan_kernels.h",
               "selective_state_space_mamba_amd/csrc/device_math.h"):
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:

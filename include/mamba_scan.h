@@ -45,6 +45,9 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; these are its only exports. */
+#define MAMBA_API __attribute__((visibility("default")))
+
 /* Return codes. */
 typedef enum {
   MAMBA_OK = 0,
@@ -105,7 +108,7 @@ typedef struct {
  * HIP call.  Returns 0 when no workspace is needed, and (size_t)-1 when the
  * arguments are invalid.  The workspace contents need not be initialised.
  */
-size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
+MAMBA_API size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
 
 /*
  * Selective-scan forward pass [MFS §6.2 Step 4 and Step 6; VIM §2.2; S4M §3].
@@ -126,7 +129,7 @@ size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
  * Errors: MAMBA_ERR_INVALID / _UNSUPPORTED / _WORKSPACE before any GPU work;
  * MAMBA_ERR_HIP if a launch is rejected.
  */
-int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+MAMBA_API int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
                    int dir_mode, void* out, float* last_state, hipStream_t stream);
 
@@ -146,12 +149,12 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
  *   out          [B][D]     dtype, written; must not alias any input
  * dims->seqlen, height, width, initial_state and workspace are ignored.
  */
-int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A,
+MAMBA_API int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A,
                     const void* B_t, const void* C_t, const float* D, const void* z_t,
                     const float* delta_bias, const mamba_dims* dims, void* out, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
-const char* mamba_status_string(int status);
+MAMBA_API const char* mamba_status_string(int status);
 
 #ifdef __cplusplus
 }

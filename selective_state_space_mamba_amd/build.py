@@ -1,23 +1,40 @@
-"""Builds libmamba_scan.so (the gfx950 HIP kernels and their C ABI) in-tree."""
+"""Builds libmamba_scan.so (the gfx950 HIP kernels and their C ABI) in-tree.
+
+The kernels are instantiated in four translation units (element type x
+input-term rule) compiled in parallel next to the host layer, then linked.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba_scan.so")
-SOURCES = [os.path.join(HERE, "csrc", "mamba_scan.hip")]
-DEPS = SOURCES + [os.path.join(HERE, "csrc", f) for f in ("scan_kernels.h", "device_math.h")] + [
+HOST = os.path.join(CSRC, "mamba_scan.hip")
+INST = os.path.join(CSRC, "scan_inst.hip")
+SOURCES = [HOST, INST]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("scan_launch.h", "scan_kernels.h", "device_math.h")] + [
     os.path.join(ROOT, "include", "mamba_scan.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# (bf16, exact) flags of the four instantiation units
+VARIANTS = [(1, 0), (1, 1), (0, 0), (0, 1)]
 
 # Packed FP32 instructions (v_pk_fma_f32 and friends) are switched off for the
 # device code; hipcc's host pass warns that it does not know the feature.
-FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-shared", "-fPIC",
+FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", os.path.join(ROOT, "include")]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n%s\n%s" % (" ".join(cmd), res.stdout))
 
 
 def build(force: bool = True, extra_flags=(), out: str | None = None) -> str:
@@ -25,12 +42,18 @@ def build(force: bool = True, extra_flags=(), out: str | None = None) -> str:
     out = out or LIB
     if not force and os.path.exists(out) and all(os.path.getmtime(out) >= os.path.getmtime(d) for d in DEPS):
         return out
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra_flags) + ["-o", tmp] + SOURCES
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + res.stdout)
-    os.replace(tmp, out)
+    with tempfile.TemporaryDirectory(prefix="mscan_build_") as tmp:
+        jobs = [[HIPCC] + FLAGS + list(extra_flags) + ["-c", "-o", os.path.join(tmp, "host.o"), HOST]]
+        for bf16, exact in VARIANTS:
+            obj = os.path.join(tmp, "inst_%d%d.o" % (bf16, exact))
+            jobs.append([HIPCC] + FLAGS + list(extra_flags) +
+                        ["-DMSCAN_INST_BF16=%d" % bf16, "-DMSCAN_INST_EXACT=%d" % exact, "-c", "-o", obj, INST])
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+            list(ex.map(_run, jobs))
+        objs = [j[j.index("-o") + 1] for j in jobs]
+        tmp_out = out + ".tmp%d" % os.getpid()
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_out] + objs)
+        os.replace(tmp_out, out)
     return out
 
 

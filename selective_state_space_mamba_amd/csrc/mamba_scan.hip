@@ -1,36 +1,16 @@
 // mamba_scan.hip -- C ABI of the gfx950 selective-scan library: argument
-// validation, the launch plan, and kernel dispatch.  The kernels live in
-// scan_kernels.h; the interface is documented in include/mamba_scan.h.
+// validation and the launch plan.  The kernels live in scan_kernels.h, their
+// launch code in scan_launch.h (instantiated by scan_inst.hip); the interface
+// is documented in include/mamba_scan.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "../../include/mamba_scan.h"
-#include "scan_kernels.h"
+#include "scan_launch.h"
 
 using namespace mscan;
 
 namespace {
-
-#ifndef MSCAN_TILE
-#define MSCAN_TILE 32
-#endif
-constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
-
-#ifndef MSCAN_TARGET_WAVES
-#define MSCAN_TARGET_WAVES 3072  // resident waves wanted: 3 per SIMD (one wave issues VALU at half rate)
-#endif
-#ifndef MSCAN_FORCE_LAYOUT
-#define MSCAN_FORCE_LAYOUT -1
-#endif
-#ifndef MSCAN_FORCE_CHUNKS
-#define MSCAN_FORCE_CHUNKS 0
-#endif
-#ifndef MSCAN_MIN_CHUNK
-#define MSCAN_MIN_CHUNK 1024     // shortest time chunk worth a separate aggregate pass
-#endif
-#ifndef MSCAN_MAX_CHUNKS
-#define MSCAN_MAX_CHUNKS 256
-#endif
 
 int num_dirs(int mode) { return mode == MAMBA_DIR_BIDIR ? 2 : mode == MAMBA_DIR_CROSS2D ? 4 : 1; }
 
@@ -44,28 +24,7 @@ int kinds_of(int mode) {
   }
 }
 
-// Workgroup layouts: CB channels per workgroup, G states per thread,
-// CB*N/G threads.  Layout 0 (64 channels, N/4 states per thread, 4 waves) is
-// the cheapest per element: the readout sums 4 partials per (token, channel)
-// and each wave's B, C reads are wave-uniform.  Layout 2 uses 16-channel
-// blocks with N/16 states per thread to spread few rows over every CU, at a
-// higher LDS cost per element.  State sizes below 16 use layout 0 only, state
-// sizes above 16 layout 2 only (at most 4 states per thread).
-struct Layout {
-  int cb, g;
-};
-constexpr Layout layout_of(int N, int id) {
-  return N < 16 ? Layout{64, N < 4 ? N : 4} : (id == 2 || N > 16) ? Layout{16, N / 16} : Layout{64, N / 4};
-}
-constexpr int threads_of(int N, int id) { return layout_of(N, id).cb * N / layout_of(N, id).g; }
-
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-struct Plan {
-  int K, Ku, layout, cb, nblk_d, nchunks, chunk_len;
-  size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
-  size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
-};
 
 // Validates the sizes (no pointers) and derives the launch plan.  A pure
 // function of dims and mode.
@@ -145,80 +104,6 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   return MAMBA_OK;
 }
 
-template <typename TIn, int N, int LID, bool EXACT>
-int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
-  constexpr Layout lay = layout_of(N, LID);
-  constexpr int NT = threads_of(N, LID);
-  if (pl.nchunks > 1) {
-    p.grid_chunks = pl.nchunks - 1;
-    const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
-  }
-  p.grid_chunks = pl.nchunks;
-  const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
-}
-
-template <typename TIn, int N, bool EXACT>
-int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
-  int rc = MAMBA_ERR_UNSUPPORTED;
-  if constexpr (N > 16) {
-    rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
-  } else if constexpr (N == 16) {
-    if (pl.layout == 2) rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
-    else rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
-  } else {
-    rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
-  }
-  if (rc != MAMBA_OK) return rc;
-  if (p.ws_y) {
-    const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
-    const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
-    hipLaunchKernelGGL((merge_dirs_kernel<TIn>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
-                       static_cast<const TIn*>(p.z), static_cast<TIn*>(p.out), p.K, rows8,
-                       (int64_t)p.Bsz * p.L * p.Dm);
-    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
-  }
-  return MAMBA_OK;
-}
-
-template <typename TIn, bool EXACT>
-int dispatch_scan(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s) {
-  switch (N) {
-    case 1: return launch_scan<TIn, 1, EXACT>(p, pl, s);
-    case 2: return launch_scan<TIn, 2, EXACT>(p, pl, s);
-    case 4: return launch_scan<TIn, 4, EXACT>(p, pl, s);
-    case 8: return launch_scan<TIn, 8, EXACT>(p, pl, s);
-    case 16: return launch_scan<TIn, 16, EXACT>(p, pl, s);
-    case 32: return launch_scan<TIn, 32, EXACT>(p, pl, s);
-    case 64: return launch_scan<TIn, 64, EXACT>(p, pl, s);
-    default: return MAMBA_ERR_UNSUPPORTED;
-  }
-}
-
-template <typename TIn, int N, bool EXACT>
-int launch_step(const StepParams& p, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((p.Bsz * p.Dm + 255) / 256);
-  hipLaunchKernelGGL((scan_step_kernel<TIn, N, EXACT>), dim3(blocks), dim3(256), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
-}
-
-template <typename TIn, bool EXACT>
-int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
-  switch (N) {
-    case 1: return launch_step<TIn, 1, EXACT>(p, s);
-    case 2: return launch_step<TIn, 2, EXACT>(p, s);
-    case 4: return launch_step<TIn, 4, EXACT>(p, s);
-    case 8: return launch_step<TIn, 8, EXACT>(p, s);
-    case 16: return launch_step<TIn, 16, EXACT>(p, s);
-    case 32: return launch_step<TIn, 32, EXACT>(p, s);
-    case 64: return launch_step<TIn, 64, EXACT>(p, s);
-    default: return MAMBA_ERR_UNSUPPORTED;
-  }
-}
-
 }  // namespace
 
 extern "C" {
@@ -273,10 +158,10 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
   p.softplus = dims->delta_softplus ? 1 : 0;
   const bool exact = dims->exact_zoh != 0;
   if (dims->dtype == MAMBA_DTYPE_BF16)
-    return exact ? dispatch_scan<uint16_t, true>(dims->dstate, p, pl, stream)
-                 : dispatch_scan<uint16_t, false>(dims->dstate, p, pl, stream);
-  return exact ? dispatch_scan<float, true>(dims->dstate, p, pl, stream)
-               : dispatch_scan<float, false>(dims->dstate, p, pl, stream);
+    return exact ? dispatch_scan_bf16_exact(dims->dstate, p, pl, stream)
+                 : dispatch_scan_bf16_simple(dims->dstate, p, pl, stream);
+  return exact ? dispatch_scan_f32_exact(dims->dstate, p, pl, stream)
+               : dispatch_scan_f32_simple(dims->dstate, p, pl, stream);
 }
 
 int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A, const void* B_t,
@@ -295,8 +180,8 @@ int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const fl
                (int)dims->batch, (int)dims->dim, dims->delta_softplus ? 1 : 0};
   const bool exact = dims->exact_zoh != 0;
   if (dims->dtype == MAMBA_DTYPE_BF16)
-    return exact ? dispatch_step<uint16_t, true>(N, p, stream) : dispatch_step<uint16_t, false>(N, p, stream);
-  return exact ? dispatch_step<float, true>(N, p, stream) : dispatch_step<float, false>(N, p, stream);
+    return exact ? dispatch_step_bf16_exact(N, p, stream) : dispatch_step_bf16_simple(N, p, stream);
+  return exact ? dispatch_step_f32_exact(N, p, stream) : dispatch_step_f32_simple(N, p, stream);
 }
 
 const char* mamba_status_string(int status) {

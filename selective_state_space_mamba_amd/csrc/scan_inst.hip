@@ -1,0 +1,38 @@
+// scan_inst.hip -- kernel instantiations and dispatchers for one element type
+// and one input-term rule, selected by the build:
+//   MSCAN_INST_BF16  = 1 (bfloat16 tensors) or 0 (float32)
+//   MSCAN_INST_EXACT = 1 (exact zero-order hold) or 0 (Δ·B·u)
+#define MSCAN_INSTANTIATE
+#include "scan_launch.h"
+
+#if !defined(MSCAN_INST_BF16) || !defined(MSCAN_INST_EXACT)
+#error "MSCAN_INST_BF16 and MSCAN_INST_EXACT must be defined"
+#endif
+
+#if MSCAN_INST_BF16
+#define MSCAN_TIN uint16_t
+#define MSCAN_T_NAME bf16
+#else
+#define MSCAN_TIN float
+#define MSCAN_T_NAME f32
+#endif
+#if MSCAN_INST_EXACT
+#define MSCAN_R_NAME exact
+#else
+#define MSCAN_R_NAME simple
+#endif
+#define MSCAN_CAT3(a, b, c) a##_##b##_##c
+#define MSCAN_NAME(a, b, c) MSCAN_CAT3(a, b, c)
+
+namespace mscan {
+
+int MSCAN_NAME(dispatch_scan, MSCAN_T_NAME, MSCAN_R_NAME)(int64_t N, const ScanParams& p, const Plan& pl,
+                                                          hipStream_t s) {
+  return dispatch_scan<MSCAN_TIN, MSCAN_INST_EXACT != 0>(N, p, pl, s);
+}
+
+int MSCAN_NAME(dispatch_step, MSCAN_T_NAME, MSCAN_R_NAME)(int64_t N, const StepParams& p, hipStream_t s) {
+  return dispatch_step<MSCAN_TIN, MSCAN_INST_EXACT != 0>(N, p, s);
+}
+
+}  // namespace mscan

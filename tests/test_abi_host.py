@@ -34,6 +34,18 @@ def test_exports_every_declared_function(lib):
         assert hasattr(lib, name), name
 
 
+def test_exports_nothing_else(lib):
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", ms.LIB_PATH], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout
+    text_syms = sorted(line.split()[-1] for line in out.splitlines() if line.split()[1:2] == ["T"])
+    assert text_syms == header_functions()
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, 7):
         assert len(ms.status_string(code)) > 0
