@@ -30,6 +30,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "scan_oracle.c")
+_CONV_SRC = os.path.join(_HERE, "conv_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -57,12 +58,13 @@ class _Inputs(ctypes.Structure):
 
 
 def build(force: bool = False) -> str:
-    """Compile scan_oracle.c into liboracle.so with gcc (no GPU code involved)."""
+    """Compile scan_oracle.c and conv_oracle.c into liboracle.so with gcc (no GPU code involved)."""
     with _lock:
-        if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in (_SRC, _CONV_SRC))
+        if force or stale:
             tmp = _LIB + ".tmp%d" % os.getpid()
             subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-                                   "-o", tmp, _SRC, "-lm"])
+                                   "-o", tmp, _SRC, _CONV_SRC, "-lm"])
             os.replace(tmp, _LIB)
     return _LIB
 
@@ -77,6 +79,10 @@ def _load():
         lib.oracle_scan_rows.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Inputs),
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_conv1d.restype = ctypes.c_int
+        lib.oracle_conv1d.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_scan_step.restype = ctypes.c_int
         lib.oracle_scan_step.argtypes = [ctypes.POINTER(_Dims)] + [ctypes.c_void_p] * 10
         lib.oracle_softplus.restype = ctypes.c_double
@@ -224,3 +230,22 @@ def silu(x: float) -> float:
 def token(dir_mode: int, k: int, p: int, seqlen: int, height: int = 0, width: int = 0) -> int:
     g = _dims(1, 1, seqlen, 1, 0, dir_mode, True, False, height, width)
     return _load().oracle_token(ctypes.byref(g), k, p)
+
+
+def conv1d(x, weight, bias=None, *, reverse=False, activation=True):
+    """Causal depthwise Conv1d + SiLU (conv_oracle.c): x [B][L][D] (float32 or
+    bfloat16 bits as uint16), weight [D][W] float32, bias [D] float32 or None.
+    Returns float64 [B][L][D]."""
+    lib = _load()
+    x = np.ascontiguousarray(x)
+    Bsz, L, Dm = x.shape
+    w = _c(weight, np.float32)
+    if w.shape[0] != Dm:
+        raise ValueError("weight must be [D][W]")
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((Bsz, L, Dm), np.float64)
+    rc = lib.oracle_conv1d(Bsz, Dm, L, _dtype_code(x), w.shape[1], 1 if reverse else 0, 1 if activation else 0,
+                           _ptr(x), _ptr(w), _ptr(b), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_conv1d: invalid arguments")
+    return out

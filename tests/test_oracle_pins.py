@@ -385,3 +385,73 @@ def test_stored_tiny_oracle_output_unchanged():
     out, st = oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"])
     got = np.concatenate([out.reshape(-1), st.reshape(-1)])
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------------------------
+# causal depthwise Conv1d + SiLU that produces u [MFS §6.2 Step 2; MFS §8 d_conv = 4;
+# VIM §2.2 (each direction convolved); S4M §3 (depthwise convolution, then SiLU)]
+
+def _conv_problem(r, Bsz=2, L=23, Dm=5, W=4):
+    x = r.standard_normal((Bsz, L, Dm)).astype(F32)
+    w = r.standard_normal((Dm, W)).astype(F32)
+    b = r.standard_normal(Dm).astype(F32)
+    return x, w, b
+
+
+def test_conv_impulse_response_is_the_taps_in_causal_order():
+    """A unit impulse at token t0 of one channel: the pre-activation output at
+    t0 + k is tap W-1-k (the last tap weighs the current token), zero before t0
+    (causal) and after t0 + W - 1."""
+    r = rng(40)
+    L, Dm, W, t0, d = 20, 3, 4, 7, 1
+    x = np.zeros((1, L, Dm), F32)
+    x[0, t0, d] = 1.0
+    w = r.standard_normal((Dm, W)).astype(F32)
+    pre = oracle.conv1d(x, w, None, activation=False)
+    want = np.zeros(L)
+    for k in range(W):
+        want[t0 + k] = w[d, W - 1 - k]
+    np.testing.assert_array_equal(pre[0, :, d], want)
+    assert np.all(pre[0, :, [0, 2]] == 0.0)
+
+
+def test_conv_matches_numpy_convolve_and_silu():
+    """Pre-activation = bias + full linear convolution with the reversed taps,
+    truncated to the first L outputs (numpy.convolve); output = z·sigmoid(z)."""
+    r = rng(41)
+    for W in (1, 2, 3, 4):
+        x, w, b = _conv_problem(r, W=W)
+        pre = oracle.conv1d(x, w, b, activation=False)
+        out = oracle.conv1d(x, w, b)
+        for bb in range(x.shape[0]):
+            for d in range(x.shape[2]):
+                ref = np.convolve(x[bb, :, d].astype(np.float64), w[d, ::-1].astype(np.float64))[: x.shape[1]]
+                np.testing.assert_allclose(pre[bb, :, d], ref + float(b[d]), rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(out, pre / (1.0 + np.exp(-pre)), rtol=1e-14, atol=0)
+
+
+def test_conv_identity_taps_and_linearity():
+    r = rng(42)
+    x, w, b = _conv_problem(r)
+    ident = np.zeros_like(w)
+    ident[:, -1] = 1.0
+    np.testing.assert_array_equal(oracle.conv1d(x, ident, None, activation=False), x.astype(np.float64))
+    x2 = r.standard_normal(x.shape).astype(F32)
+    lhs = oracle.conv1d((x + x2).astype(F32), w, None, activation=False)
+    rhs = oracle.conv1d(x, w, None, activation=False) + oracle.conv1d(x2, w, None, activation=False)
+    # x + x2 is rounded to float32 before the convolution
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-5)
+
+
+def test_conv_reverse_is_flipped_forward():
+    r = rng(43)
+    x, w, b = _conv_problem(r)
+    fwd_of_flip = oracle.conv1d(np.ascontiguousarray(x[:, ::-1]), w, b)
+    np.testing.assert_array_equal(oracle.conv1d(x, w, b, reverse=True), fwd_of_flip[:, ::-1])
+
+
+def test_conv_bf16_inputs_widen_exactly():
+    r = rng(44)
+    x, w, b = _conv_problem(r)
+    xb = I.bf16_bits(x)
+    np.testing.assert_array_equal(oracle.conv1d(xb, w, b), oracle.conv1d(I.bf16_to_f32(xb), w, b))
