@@ -153,6 +153,27 @@ MAMBA_API int mamba_scan_step(float* state, const void* u_t, const void* delta_t
                     const void* B_t, const void* C_t, const float* D, const void* z_t,
                     const float* delta_bias, const mamba_dims* dims, void* out, hipStream_t stream);
 
+/*
+ * Causal depthwise Conv1d followed by SiLU, the step that produces the scan
+ * input u from the expanded activations [MFS §6.2 Step 2 (a small depthwise
+ * causal 1-D convolution before the SSM); MFS §8 (d_conv = 4); VIM §2.2 (each
+ * direction convolved on its own); S4M §3 (depthwise convolution, then SiLU)].
+ * For batch b, channel d and sequence position s, with W = width taps:
+ *   out(s) = silu(bias[d] + Σ_{j=0}^{W-1} weight[d][j]·x(s - (W-1) + j)),
+ *   x(s) = 0 for s < 0 (tap W-1 weighs the current token),
+ * where s is the token index t, or L-1-t when reverse is nonzero (the
+ * convolution runs along the reversed sequence, as for a backward scan).
+ *   x       [B][L][D]  dtype
+ *   weight  [D][W]     float32 (a depthwise Conv1d weight [D][1][W] without its middle axis)
+ *   bias    [D]        float32 or NULL
+ *   out     [B][L][D]  dtype, written; must not alias x
+ * Uses dims->batch, dim, seqlen and dtype only.  Errors: MAMBA_ERR_INVALID
+ * (NULL pointer, size <= 0, unknown dtype), MAMBA_ERR_UNSUPPORTED (width above
+ * 4, dim not a multiple of 8, x or out not 16-byte aligned), MAMBA_ERR_HIP.
+ */
+MAMBA_API int mamba_conv1d_silu(const void* x, const float* weight, const float* bias, const mamba_dims* dims,
+                                int width, int reverse, void* out, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 MAMBA_API const char* mamba_status_string(int status);
 

@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmamba_scan.so")
 MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP = 0, -1, -2, -3, -4
 DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-EXPORTED = ("mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step", "mamba_status_string")
+EXPORTED = ("mamba_conv1d_silu", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step",
+            "mamba_status_string")
 
 
 class MambaDims(ctypes.Structure):
@@ -54,6 +55,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), i32, vp, vp, vp]
     lib.mamba_scan_step.restype = i32
     lib.mamba_scan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), vp, vp]
+    lib.mamba_conv1d_silu.restype = i32
+    lib.mamba_conv1d_silu.argtypes = [vp, vp, vp, ctypes.POINTER(MambaDims), i32, i32, vp, vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
     lib.mamba_status_string.argtypes = [i32]
     _lib = lib
@@ -197,4 +200,28 @@ def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=Non
                              _ptr(z_t), _ptr(delta_bias), ctypes.byref(dims), _ptr(out), _stream(stream))
     if rc != MAMBA_OK:
         raise MambaError(rc, "mamba_scan_step")
+    return out
+
+
+def conv1d_silu(x, weight, bias=None, *, reverse=False, out=None, stream=None):
+    """mamba_conv1d_silu on torch tensors: x [B][L][D] (bfloat16 or float32),
+    weight [D][W] float32, bias [D] float32 or None.  Returns out [B][L][D]."""
+    import torch
+    lib = load_library()
+    dev = x.device
+    Bsz, L, Dm = x.shape
+    if weight.dim() != 2 or weight.shape[0] != Dm:
+        raise ValueError("weight must be [D][W], got %s" % (tuple(weight.shape),))
+    W = weight.shape[1]
+    _check(weight, "weight", (Dm, W), torch.float32, dev)
+    _check(bias, "bias", (Dm,), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _check(out, "out", (Bsz, L, Dm), x.dtype, dev)
+    _check(x, "x", (Bsz, L, Dm), x.dtype, dev)
+    dims = make_dims(Bsz, Dm, L, 1, _dtype_code(x))
+    rc = lib.mamba_conv1d_silu(_ptr(x), _ptr(weight), _ptr(bias), ctypes.byref(dims), int(W), 1 if reverse else 0,
+                               _ptr(out), _stream(stream))
+    if rc != MAMBA_OK:
+        raise MambaError(rc, "mamba_conv1d_silu")
     return out

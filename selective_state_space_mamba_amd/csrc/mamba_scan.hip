@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/mamba_scan.h"
+#include "conv_kernels.h"
 #include "scan_launch.h"
 
 using namespace mscan;
@@ -104,6 +105,28 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   return MAMBA_OK;
 }
 
+
+constexpr int kConvRun = 32;  // positions per thread of the Conv1d kernel
+
+template <typename TIn, int W>
+int launch_conv(const ConvParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.Bsz * ((p.L + kConvRun - 1) / kConvRun) * (p.Dm / 8);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  hipLaunchKernelGGL((conv1d_silu_kernel<TIn, W, kConvRun>), dim3(blocks), dim3(256), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TIn>
+int dispatch_conv(int width, const ConvParams& p, hipStream_t stream) {
+  switch (width) {
+    case 1: return launch_conv<TIn, 1>(p, stream);
+    case 2: return launch_conv<TIn, 2>(p, stream);
+    case 3: return launch_conv<TIn, 3>(p, stream);
+    case 4: return launch_conv<TIn, 4>(p, stream);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,6 +205,22 @@ int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const fl
   if (dims->dtype == MAMBA_DTYPE_BF16)
     return exact ? dispatch_step_bf16_exact(N, p, stream) : dispatch_step_bf16_simple(N, p, stream);
   return exact ? dispatch_step_f32_exact(N, p, stream) : dispatch_step_f32_simple(N, p, stream);
+}
+
+int mamba_conv1d_silu(const void* x, const float* weight, const float* bias, const mamba_dims* dims, int width,
+                      int reverse, void* out, hipStream_t stream) {
+  if (!dims || !x || !weight || !out) return MAMBA_ERR_INVALID;
+  if (dims->dtype != MAMBA_DTYPE_F32 && dims->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID;
+  if (dims->batch <= 0 || dims->dim <= 0 || dims->seqlen <= 0 || width <= 0) return MAMBA_ERR_INVALID;
+  if (width > 4 || dims->dim % 8 != 0) return MAMBA_ERR_UNSUPPORTED;
+  if (dims->seqlen > INT32_MAX / 2 || dims->dim > INT32_MAX / 2 || dims->batch > INT32_MAX / 2 ||
+      dims->batch * ((dims->seqlen + kConvRun - 1) / kConvRun) * (dims->dim / 8) > (int64_t)INT32_MAX * 64)
+    return MAMBA_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(out) || ((uintptr_t)weight & 3u) || (bias && ((uintptr_t)bias & 3u)))
+    return MAMBA_ERR_UNSUPPORTED;
+  ConvParams p{x, weight, bias, out, (int)dims->batch, (int)dims->seqlen, (int)dims->dim, reverse ? 1 : 0};
+  if (dims->dtype == MAMBA_DTYPE_BF16) return dispatch_conv<uint16_t>(width, p, stream);
+  return dispatch_conv<float>(width, p, stream);
 }
 
 const char* mamba_status_string(int status) {

@@ -117,3 +117,15 @@ def make_inputs(w: Workload, seqlen: int | None = None) -> dict:
         A, D, delta_bias = A.reshape(Dm, N), D.reshape(Dm), delta_bias.reshape(Dm)
     return dict(u=u, delta=delta, z=z if w.gated else None, B=B, C=C, A=A, D=D,
                 delta_bias=delta_bias)
+
+
+def make_conv_inputs(batch: int, seqlen: int, dim: int, width: int, dtype: str, seed: int) -> dict:
+    """Inputs of the causal depthwise Conv1d + SiLU prologue: x [B][L][D] standard
+    normal (rounded to bf16 for bf16), weight [D][W] and bias [D] uniform in
+    ±1/sqrt(W) (the default initialisation of a depthwise Conv1d, fan-in W)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _normal(rng, (batch, seqlen, dim), dtype)
+    bound = 1.0 / np.sqrt(width)
+    weight = rng.uniform(-bound, bound, size=(dim, width)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=dim).astype(np.float32)
+    return dict(x=x, weight=weight, bias=bias)

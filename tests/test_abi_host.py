@@ -16,7 +16,7 @@ FAKE = 0x100000  # 16-byte aligned stand-in pointer: every call below fails vali
 def header_functions():
     src = open(os.path.join(ROOT, "include", "mamba_scan.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -117,3 +117,19 @@ def test_step_validation(lib):
     assert step(dims(), B=FAKE + 8) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert lib.mamba_scan_step(None, None, None, None, None, None, None, None, None, None, None, None) == \
         ms._binding.MAMBA_ERR_INVALID
+
+
+def test_conv1d_validation(lib):
+    d = dims(dim=64, seqlen=10)
+    conv = lambda dd, width=4, x=FAKE, w=FAKE, b=None, out=FAKE: lib.mamba_conv1d_silu(
+        x, w, b, ctypes.byref(dd), width, 0, out, None)
+    assert conv(d, x=None) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(d, w=None) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(d, out=None) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(d, width=0) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(dims(dim=64, seqlen=0)) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(dims(dim=64, dtype=7)) == ms._binding.MAMBA_ERR_INVALID
+    assert conv(d, width=5) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert conv(dims(dim=60)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert conv(d, x=FAKE + 8) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert conv(d, w=FAKE + 2) == ms._binding.MAMBA_ERR_UNSUPPORTED
