@@ -5,10 +5,12 @@ written), inputs already resident in HBM.
 
 Prints one JSON line.  `value` is scan elements (B·D·L·N) per second over the
 timed steps.  `roofline` describes the scan kernel: it is bound by vector-ALU
-issue (every element needs one v_exp_f32, which issues at half rate, and four
-fp32 VALU operations), so the bound reported is "alu" in elements/s, with the
+issue (every element needs one v_exp_f32, at a quarter of the fp32 rate, and
+four fp32 operations), so the bound reported is "alu" in elements/s, with the
 HBM view alongside.  `cpu_baseline` times the fp64 CPU oracle on a bounded
-sample of the same workload.
+sample of the same workload.  `conv1d` times the causal depthwise Conv1d + SiLU
+prologue on the layer's activations against the HBM peak (it is bandwidth
+bound).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--decode-steps S]
@@ -28,12 +30,16 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# Vector-ALU issue model of MI355X (gfx950): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-# = 39.32e12 lane-instructions/s.  Per scan element the method needs Δ·A, Δu·B, the
-# state FMA and the readout FMA (4 VALU) plus exp (v_exp_f32, 2 issue slots at half rate).
-VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
-SLOTS_PER_ELEMENT = 6.0
-ALU_PEAK_ELEM = VALU_LANE_OPS / SLOTS_PER_ELEMENT
+# Vector-ALU peak of MI355X (gfx950) for this method.  The published fp32 vector
+# rate, 157.3 TFLOP/s, is 78.6e12 fp32 lane-operations/s (an FMA counts two flops):
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz, one 64-lane fp32 add/mul/FMA per 2 cycles
+# per SIMD, which is what these instructions measure on the chip.  v_exp_f32 issues
+# at a quarter of that rate (measured: 8 cycles per 64-lane instruction).  Each
+# scan element needs four fp32 operations (Δ'·A, Δu·B, the state FMA, the readout
+# FMA) and one exp: 4/78.6e12 + 1/19.7e12 s, i.e. 9.83e12 elements/s.
+FP32_LANE_OPS = 256 * 4 * 32 * 2.4e9
+EXP_LANE_OPS = FP32_LANE_OPS / 4
+ALU_PEAK_ELEM = 1.0 / (4.0 / FP32_LANE_OPS + 1.0 / EXP_LANE_OPS)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -121,6 +127,7 @@ def main():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512)
+    ap.add_argument("--conv-steps", type=int, default=20, help="timed calls of the Conv1d + SiLU prologue (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one torch elementwise kernel that reads and writes a "
                          "MIB-MiB buffer (known bytes, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -216,6 +223,33 @@ def main():
         decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
                   "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4}
 
+    conv = None
+    if args.conv_steps > 0 and w.dir_mode == 0:
+        W = 4
+        cxs = [{k: todev(v) for k, v in I.make_conv_inputs(w.batch, w.seqlen, w.dim, W, w.dtype,
+                                                           w.seed + 77 + s_).items()} for s_ in range(len(sets))]
+        couts = [torch.empty_like(c["x"]) for c in cxs]
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                ms.conv1d_silu(cxs[i % len(cxs)]["x"], cxs[i % len(cxs)]["weight"], cxs[i % len(cxs)]["bias"],
+                               out=couts[i % len(cxs)], stream=stream)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.conv_steps)]
+            for i in range(args.conv_steps):
+                c = cxs[i % len(cxs)]
+                evs[i][0].record(stream)
+                ms.conv1d_silu(c["x"], c["weight"], c["bias"], out=couts[i % len(cxs)], stream=stream)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+        conv_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        e = 2 if w.dtype == "bf16" else 4
+        cbytes = 2 * w.batch * w.seqlen * w.dim * e + w.dim * (W + 1) * 4
+        conv = {"op": "causal depthwise Conv1d (%d taps) + SiLU, [B][L][D] = [%d][%d][%d] %s"
+                      % (W, w.batch, w.seqlen, w.dim, w.dtype),
+                "us_per_call": conv_s * 1e6, "algorithmic_bytes": cbytes, "achieved_gbs": cbytes / conv_s / 1e9,
+                "peak_gbs": HBM_PEAK_GBS, "frac": cbytes / conv_s / 1e9 / HBM_PEAK_GBS, "bound": "hbm"}
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -250,6 +284,7 @@ def main():
                              "algorithmic_bytes": alg_bytes}},
         "cpu_baseline": cpu,
         "decode": decode,
+        "conv1d": conv,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)
