@@ -59,7 +59,7 @@ __global__ void __launch_bounds__(256) conv1d_silu_kernel(const ConvParams p) {
   auto row = [&](int s) { return (int64_t)(p.reverse ? L - 1 - s : s) * p.Dm; };
 
   // Before output position s: win[j] holds position s - W + j for j >= 1; each
-  // step shifts the window down one slot and loads position s into slot W-1,
+  // step shifts the window down one slot and takes position s into slot W-1,
   // so that win[j] holds position s - (W-1) + j while s is computed.
   float win[W][V];
 #pragma unroll
@@ -75,26 +75,38 @@ __global__ void __launch_bounds__(256) conv1d_silu_kernel(const ConvParams p) {
       for (int c = 0; c < V; ++c) win[j][c] = 0.f;
     }
   }
+  // Rows arrive in groups of RG, the next group's loads issued before the
+  // current group is computed.  Rows past the end are clamped to the last row
+  // (their outputs are not stored), so the loads carry no branch.
+  constexpr int RG = T < 8 ? T : 8;
+  static_assert(T % RG == 0, "whole row groups");
+  Vec<TIn, V> rows[2][RG];
+  auto load_group = [&](int g, Vec<TIn, V>(&dst)[RG]) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < T; ++k) {
-    const int s = s0 + k;
-    if (s >= L) break;
+    for (int r = 0; r < RG; ++r) dst[r].load(xb + row(min(s0 + g * RG + r, L - 1)));
+  };
+  load_group(0, rows[0]);
 #pragma unroll
-    for (int j = 0; j + 1 < W; ++j)
+  for (int g = 0; g < T / RG; ++g) {
+    if (g + 1 < T / RG) load_group(g + 1, rows[(g + 1) & 1]);
 #pragma unroll
-      for (int c = 0; c < V; ++c) win[j][c] = win[j + 1][c];
-    Vec<TIn, V> v;
-    v.load(xb + row(s));
-    float y[V];
+    for (int r = 0; r < RG; ++r) {
+      const int s = s0 + g * RG + r;
 #pragma unroll
-    for (int c = 0; c < V; ++c) {
-      win[W - 1][c] = v.get(c);
-      float acc = bias[c];
+      for (int j = 0; j + 1 < W; ++j)
 #pragma unroll
-      for (int j = 0; j < W; ++j) acc = __builtin_fmaf(w[j][c], win[j][c], acc);
-      y[c] = silu_f(acc);
+        for (int c = 0; c < V; ++c) win[j][c] = win[j + 1][c];
+      float y[V];
+#pragma unroll
+      for (int c = 0; c < V; ++c) {
+        win[W - 1][c] = rows[g & 1][r].get(c);
+        float acc = bias[c];
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc = __builtin_fmaf(w[j][c], win[j][c], acc);
+        y[c] = silu_f(acc);
+      }
+      if (s < L) storeV<V>(ob + row(s), y);
     }
-    storeV<V>(ob + row(s), y);
   }
 }
 

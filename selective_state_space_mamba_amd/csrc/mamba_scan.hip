@@ -106,7 +106,10 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 }
 
 
-constexpr int kConvRun = 32;  // positions per thread of the Conv1d kernel
+#ifndef MSCAN_CONV_RUN
+#define MSCAN_CONV_RUN 16
+#endif
+constexpr int kConvRun = MSCAN_CONV_RUN;  // positions per thread of the Conv1d kernel
 
 template <typename TIn, int W>
 int launch_conv(const ConvParams& p, hipStream_t stream) {
