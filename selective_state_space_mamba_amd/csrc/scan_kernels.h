@@ -254,12 +254,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int tt = ng * TPT + i;
-      const bool ok = (p0 + tt < pend) && dvalid;
-      // branch-free: compute on whatever the registers hold, then select
+      // Branch-free: compute on whatever the registers hold (finite values of
+      // clamped rows and channels), then zero rows past the chunk end and
+      // channels past D by a 0/1 factor -- cheaper than a select per value.
+      const float okf = ((p0 + tt < pend) && dvalid) ? 1.f : 0.f;
       const float x = to_f32(r.dl[i]) + bias;
-      const float sp = softplus_log2(x);
-      const float dl = ok ? (p.softplus ? sp : x * kLog2e) : 0.f;  // Δ' = Δ·log2 e
-      const float uu = ok ? to_f32(r.u[i]) : 0.f;
+      const float dl = (p.softplus ? softplus_log2(x) : x * kLog2e) * okf;  // Δ' = Δ·log2 e
+      const float uu = to_f32(r.u[i]) * okf;
       dd[2 * i] = dl;
       dd[2 * i + 1] = EXACT ? uu : dl * uu;
       if constexpr (!AGG) {
@@ -276,11 +277,12 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       const int q = tid + i * NT;
       if (q < BCU) {
         const int tt = q / UPR, nq = q % UPR;
-        const bool okq = p0 + tt < pend;
+        const float okq = p0 + tt < pend ? 1.f : 0.f;
+        const float bscale = okq * (EXACT ? 1.f : kLn2);  // Δ·B = Δ'·(B·ln 2)
 #pragma unroll
         for (int e = 0; e < EQ; ++e) {
-          s_B[(nq * EQ + e) * BS + tt] = okq ? r.B[i].get(e) * (EXACT ? 1.f : kLn2) : 0.f;  // Δ·B = Δ'·(B·ln 2)
-          if constexpr (!AGG) s_C[(nq * EQ + e) * BS + tt] = okq ? r.C[i].get(e) : 0.f;
+          s_B[(nq * EQ + e) * BS + tt] = r.B[i].get(e) * bscale;
+          if constexpr (!AGG) s_C[(nq * EQ + e) * BS + tt] = r.C[i].get(e) * okq;
         }
       }
     }
