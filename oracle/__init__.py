@@ -79,6 +79,9 @@ def _load():
         lib.oracle_scan_rows.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Inputs),
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_scan_bwd.restype = ctypes.c_int
+        lib.oracle_scan_bwd.argtypes = [ctypes.POINTER(_Dims), ctypes.POINTER(_Inputs), ctypes.c_void_p] + \
+            [ctypes.c_void_p] * 9
         lib.oracle_conv1d.restype = ctypes.c_int
         lib.oracle_conv1d.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -248,4 +251,43 @@ def conv1d(x, weight, bias=None, *, reverse=False, activation=True):
                            _ptr(x), _ptr(w), _ptr(b), _ptr(out))
     if rc != 0:
         raise ValueError("oracle_conv1d: invalid arguments")
+    return out
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, dout=None, *, dir_mode=DIR_FWD, height=0,
+             width=0, delta_softplus=True, exact_zoh=False, initial_state=None):
+    """Gradients of L = sum(dout * out) with respect to every input of ``scan``
+    (oracle_scan_bwd, float64).  Same layouts as ``scan``; dout is [B][L][D] in
+    the input type.  Returns a dict of float64 arrays shaped like the inputs:
+    du, ddelta, dA, dB, dC, dD, dz (None without z), ddelta_bias, dinit."""
+    lib = _load()
+    K = num_dirs(dir_mode)
+    u = _c(u)
+    dt = _dtype_code(u)
+    delta, B, C, z, dout = (_c(x) for x in (delta, B, C, z, dout))
+    for x in (delta, B, C, dout) + ((z,) if z is not None else ()):
+        if x.dtype != u.dtype:
+            raise TypeError("u, delta, B, C, z, dout must share one dtype")
+    A = _c(A, np.float32)
+    D = _c(D, np.float32)
+    delta_bias = _c(delta_bias, np.float32)
+    initial_state = _c(initial_state, np.float32)
+    Bsz, L, Dm, N = u.shape[0], delta.shape[-2], delta.shape[-1], B.shape[-1]
+    Ku = 1 if dir_mode == DIR_CROSS2D else K
+    if dout.size != Bsz * L * Dm:
+        raise ValueError("dout must be [B][L][D]")
+    g = _dims(Bsz, Dm, L, N, dt, dir_mode, delta_softplus, exact_zoh, height, width)
+    ins = _Inputs(_ptr(u), _ptr(delta), _ptr(B), _ptr(C), _ptr(z), _ptr(A), _ptr(D),
+                  _ptr(delta_bias), _ptr(initial_state))
+    kx = () if K == 1 else (K,)
+    ux = () if Ku == 1 else (Ku,)
+    out = dict(du=np.empty((Bsz,) + ux + (L, Dm)), ddelta=np.empty((Bsz,) + kx + (L, Dm)),
+               dA=np.empty(kx + (Dm, N)), dB=np.empty((Bsz,) + kx + (L, N)), dC=np.empty((Bsz,) + kx + (L, N)),
+               dD=np.empty(kx + (Dm,)), dz=None if z is None else np.empty((Bsz, L, Dm)),
+               ddelta_bias=np.empty(kx + (Dm,)), dinit=np.empty((Bsz,) + kx + (Dm, N)))
+    rc = lib.oracle_scan_bwd(ctypes.byref(g), ctypes.byref(ins), _ptr(dout), _ptr(out["du"]), _ptr(out["ddelta"]),
+                             _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]),
+                             _ptr(out["ddelta_bias"]), _ptr(out["dinit"]))
+    if rc != 0:
+        raise ValueError("oracle_scan_bwd failed with %d" % rc)
     return out

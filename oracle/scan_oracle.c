@@ -240,3 +240,147 @@ int oracle_scan_step(const oracle_dims* g, double* state, const void* u_t, const
     }
   return 0;
 }
+
+/*
+ * Gradients of the forward scan, by reverse-mode differentiation in fp64.
+ * For a loss L = Σ dout·out (dout = dL/dout, [B][L][D]) it returns dL/d of
+ * every input.  The pages run the backward pass of the fused kernel by
+ * recomputing the states [MFS §5; S4M §2.3]; here every state is simply
+ * recomputed in full.  Per direction k, batch b, channel d and state n, with
+ * scan position p visiting token t and h_{-1} the initial state:
+ *   y_all[t] = Σ_k y_k[t];  g = silu(z);  dy = dout·g;  dz = dout·y_all·silu'(z)
+ *   λ_p = C_t[n]·dy_t + Ā_{p+1}·λ_{p+1}  (λ_L = 0)   -- the adjoint of h_p
+ *   dL/dĀ_p = λ_p·h_{p-1},  dL/d(B̄u)_p = λ_p
+ *   Ā = e^{ΔA}; simplified rule B̄u = Δ·B·u; exact rule B̄u = c·B·u with
+ *     c = (Ā - 1)/A, dc/dΔ = Ā, dc/dA = (Δ·Ā - c)/A  (c = Δ, dc/dA = Δ²/2 at A = 0)
+ *   dΔ_p += λ h_{p-1} A Ā + λ (dc/dΔ or 1)·B·u;  dA += λ h_{p-1} Δ Ā (+ λ (dc/dA) B u, exact)
+ *   dB_t += λ·(c or Δ)·u;  du_t += λ·(c or Δ)·B;  dC_t += dy_t·h_p
+ *   du_t += D·dy_t;  dD += dy_t·u_t
+ *   dx = dΔ·σ(x) with softplus (dx = dΔ without);  ddelta = dx;  ddelta_bias += dx
+ *   dinit = Ā_0·λ_0
+ * Outputs (double, zeroed here): du [B][Ku][L][D], ddelta [B][K][L][D],
+ * dA [K][D][N], dB, dC [B][K][L][N], dD [K][D], dz [B][L][D] (may be NULL when
+ * z is NULL), ddelta_bias [K][D], dinit [B][K][D][N].
+ * Returns 0, -1 on invalid arguments, -2 on allocation failure.
+ */
+int oracle_scan_bwd(const oracle_dims* g, const oracle_inputs* in, const void* dout, double* du, double* ddelta,
+                    double* dA, double* dB, double* dC, double* dD, double* dz, double* ddelta_bias, double* dinit) {
+  if (!g || !in || !in->u || !in->delta || !in->A || !in->B || !in->C || !dout) return -1;
+  if (!du || !ddelta || !dA || !dB || !dC || !dD || !ddelta_bias || !dinit || (in->z && !dz)) return -1;
+  if (g->batch <= 0 || g->dim <= 0 || g->seqlen <= 0 || g->dstate <= 0) return -1;
+  const int K = oracle_num_dirs(g->dir_mode);
+  if (K == 0) return -1;
+  if (g->dir_mode == 3 && (g->height <= 0 || g->width <= 0 || g->height * g->width != g->seqlen)) return -1;
+  const int64_t Bn = g->batch, L = g->seqlen, Dm = g->dim, N = g->dstate;
+  const int Ku = (g->dir_mode == 3) ? 1 : K;
+  memset(du, 0, sizeof(double) * (size_t)(Bn * Ku * L * Dm));
+  memset(ddelta, 0, sizeof(double) * (size_t)(Bn * K * L * Dm));
+  memset(dA, 0, sizeof(double) * (size_t)(K * Dm * N));
+  memset(dB, 0, sizeof(double) * (size_t)(Bn * K * L * N));
+  memset(dC, 0, sizeof(double) * (size_t)(Bn * K * L * N));
+  memset(dD, 0, sizeof(double) * (size_t)(K * Dm));
+  if (dz) memset(dz, 0, sizeof(double) * (size_t)(Bn * L * Dm));
+  memset(ddelta_bias, 0, sizeof(double) * (size_t)(K * Dm));
+  memset(dinit, 0, sizeof(double) * (size_t)(Bn * K * Dm * N));
+  /* per row: states h[p][n] after step p, decays a[p][n], Δ, x and u per position */
+  double* hs = (double*)malloc(sizeof(double) * (size_t)(K * L * N));
+  double* as = (double*)malloc(sizeof(double) * (size_t)(K * L * N));
+  double* dts = (double*)malloc(sizeof(double) * (size_t)(K * L));
+  double* xs = (double*)malloc(sizeof(double) * (size_t)(K * L));
+  double* vs = (double*)malloc(sizeof(double) * (size_t)(K * L));
+  double* yall = (double*)malloc(sizeof(double) * (size_t)L);
+  double* dy = (double*)malloc(sizeof(double) * (size_t)L);
+  double* lam = (double*)malloc(sizeof(double) * (size_t)N);
+  double* h0 = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!hs || !as || !dts || !xs || !vs || !yall || !dy || !lam || !h0) {
+    free(hs); free(as); free(dts); free(xs); free(vs); free(yall); free(dy); free(lam); free(h0);
+    return -2;
+  }
+  for (int64_t b = 0; b < Bn; ++b) {
+    for (int64_t d = 0; d < Dm; ++d) {
+      /* forward, keeping every state */
+      for (int64_t t = 0; t < L; ++t) yall[t] = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const int ku = (Ku == 1) ? 0 : k;
+        const double bias = in->delta_bias ? (double)in->delta_bias[k * Dm + d] : 0.0;
+        const double Dk = in->D ? (double)in->D[k * Dm + d] : 0.0;
+        for (int64_t n = 0; n < N; ++n)
+          h0[n] = in->initial_state ? (double)in->initial_state[((b * K + k) * Dm + d) * N + n] : 0.0;
+        for (int64_t p = 0; p < L; ++p) {
+          const int64_t t = oracle_token(g, k, p);
+          const double x = ld(in->delta, g->dtype, ((b * K + k) * L + t) * Dm + d) + bias;
+          const double dt = g->delta_softplus ? oracle_softplus(x) : x;
+          const double v = ld(in->u, g->dtype, ((b * Ku + ku) * L + t) * Dm + d);
+          xs[k * L + p] = x;
+          dts[k * L + p] = dt;
+          vs[k * L + p] = v;
+          const int64_t bc = ((b * K + k) * L + t) * N;
+          double y = Dk * v;
+          for (int64_t n = 0; n < N; ++n) {
+            const double An = (double)in->A[(k * Dm + d) * N + n];
+            const double a = exp(dt * An);
+            const double c = (g->exact_zoh && An != 0.0) ? (a - 1.0) / An : dt;
+            const double hp = p > 0 ? hs[(k * L + p - 1) * N + n] : h0[n];
+            const double hn = a * hp + c * ld(in->B, g->dtype, bc + n) * v;
+            as[(k * L + p) * N + n] = a;
+            hs[(k * L + p) * N + n] = hn;
+            y += ld(in->C, g->dtype, bc + n) * hn;
+          }
+          yall[t] += y;
+        }
+      }
+      /* gate */
+      for (int64_t t = 0; t < L; ++t) {
+        const double go = ld(dout, g->dtype, (b * L + t) * Dm + d);
+        if (in->z) {
+          const double zz = ld(in->z, g->dtype, (b * L + t) * Dm + d);
+          const double sg = 1.0 / (1.0 + exp(-zz));
+          dy[t] = go * zz * sg;
+          dz[(b * L + t) * Dm + d] = go * yall[t] * sg * (1.0 + zz * (1.0 - sg));
+        } else {
+          dy[t] = go;
+        }
+      }
+      /* reverse pass of each direction */
+      for (int k = 0; k < K; ++k) {
+        const int ku = (Ku == 1) ? 0 : k;
+        const double Dk = in->D ? (double)in->D[k * Dm + d] : 0.0;
+        for (int64_t n = 0; n < N; ++n) lam[n] = 0.0;
+        for (int64_t n = 0; n < N; ++n)
+          h0[n] = in->initial_state ? (double)in->initial_state[((b * K + k) * Dm + d) * N + n] : 0.0;
+        for (int64_t p = L - 1; p >= 0; --p) {
+          const int64_t t = oracle_token(g, k, p);
+          const double dt = dts[k * L + p], v = vs[k * L + p], x = xs[k * L + p];
+          const int64_t bc = ((b * K + k) * L + t) * N;
+          double ddt = 0.0, duv = Dk * dy[t];
+          dD[k * Dm + d] += dy[t] * v;
+          for (int64_t n = 0; n < N; ++n) {
+            const double An = (double)in->A[(k * Dm + d) * N + n];
+            const double a = as[(k * L + p) * N + n];
+            const double hp = p > 0 ? hs[(k * L + p - 1) * N + n] : h0[n];
+            const double Bv = ld(in->B, g->dtype, bc + n);
+            const double Cv = ld(in->C, g->dtype, bc + n);
+            const double l = Cv * dy[t] + lam[n]; /* lam[n] holds Ā_{p+1}·λ_{p+1} */
+            const int exact = g->exact_zoh;
+            const double c = (exact && An != 0.0) ? (a - 1.0) / An : dt;
+            const double dc_ddt = exact ? a : 1.0;
+            const double dc_dA = !exact ? 0.0 : (An != 0.0 ? (dt * a - c) / An : 0.5 * dt * dt);
+            ddt += l * hp * An * a + l * dc_ddt * Bv * v;
+            dA[(k * Dm + d) * N + n] += l * hp * dt * a + l * dc_dA * Bv * v;
+            dB[bc + n] += l * c * v;
+            dC[bc + n] += dy[t] * hs[(k * L + p) * N + n];
+            duv += l * c * Bv;
+            lam[n] = a * l;
+          }
+          du[((b * Ku + ku) * L + t) * Dm + d] += duv;
+          const double dx = g->delta_softplus ? ddt / (1.0 + exp(-x)) : ddt;
+          ddelta[((b * K + k) * L + t) * Dm + d] = dx;
+          ddelta_bias[k * Dm + d] += dx;
+        }
+        for (int64_t n = 0; n < N; ++n) dinit[((b * K + k) * Dm + d) * N + n] = lam[n];
+      }
+    }
+  }
+  free(hs); free(as); free(dts); free(xs); free(vs); free(yall); free(dy); free(lam); free(h0);
+  return 0;
+}
