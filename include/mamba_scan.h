@@ -174,6 +174,45 @@ MAMBA_API int mamba_scan_step(float* state, const void* u_t, const void* delta_t
 MAMBA_API int mamba_conv1d_silu(const void* x, const float* weight, const float* bias, const mamba_dims* dims,
                                 int width, int reverse, void* out, hipStream_t stream);
 
+/*
+ * Bytes of device workspace mamba_scan_bwd needs for these dims and mode.  A
+ * pure function of its arguments; (size_t)-1 when the arguments are invalid
+ * or the backward pass is not built for them.  The workspace is never 0.
+ */
+MAMBA_API size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
+
+/*
+ * Selective-scan backward pass: gradients of a loss with respect to every
+ * input of mamba_scan_fwd, given dout = ∂loss/∂out [MFS §5 and S4M §2.3: the
+ * training pass keeps only the inputs and recomputes the states].  Same
+ * inputs, layouts, dims and dir_mode as mamba_scan_fwd (dims->initial_state,
+ * if set, is the state the forward started from); the gradients have the
+ * layout and element type of their input:
+ *   dout         [B][L][D]    dtype (read)
+ *   du           [B][Ku][L][D] dtype   (the cross scan sums its four directions)
+ *   ddelta       [B][K][L][D]  dtype   (with respect to delta before bias and softplus)
+ *   dA           [K][D][N]     float32
+ *   dB, dC       [B][K][L][N]  dtype
+ *   dD           [K][D]        float32, or NULL: not computed
+ *   dz           [B][L][D]     dtype,   or NULL: not computed (ignored without z)
+ *   ddelta_bias  [K][D]        float32, or NULL: not computed
+ *   dinit        [B][K][D][N]  float32, or NULL: gradient of the initial state
+ * Per direction, with λ the adjoint of the state (λ = C·dy + Ā_next·λ_next
+ * backwards over the scan order) and dy = dout·silu(z):
+ *   du = Σ_n λ·c·B + D·dy,  dΔ = Σ_n λ·(A·Ā·h_prev + (∂c/∂Δ)·B·u),
+ *   dA = Σ λ·(Δ·Ā·h_prev + (∂c/∂A)·B·u),  dB = Σ_d λ·c·u,  dC = Σ_d dy·h,
+ *   dD = Σ dy·u,  dz = dout·(Σ_k y_k)·silu'(z),  ddelta = dΔ·sigmoid(delta + bias)
+ * (c = Δ, or (Ā - 1)/A with exact_zoh).  The gradient outputs must not alias
+ * any input or each other.  Built for dstate N in 1..16; N = 32 or 64 gives
+ * MAMBA_ERR_UNSUPPORTED.  dims->workspace must hold
+ * mamba_scan_bwd_workspace_bytes() bytes; its contents need not be
+ * initialised.  Errors as for mamba_scan_fwd.
+ */
+MAMBA_API int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, const void* dout,
+                             const mamba_dims* dims, int dir_mode, void* du, void* ddelta, float* dA, void* dB,
+                             void* dC, float* dD, void* dz, float* ddelta_bias, float* dinit, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 MAMBA_API const char* mamba_status_string(int status);
 

@@ -16,8 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmamba_scan.so")
 MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP = 0, -1, -2, -3, -4
 DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
-EXPORTED = ("mamba_conv1d_silu", "mamba_scan_fwd_workspace_bytes", "mamba_scan_fwd", "mamba_scan_step",
-            "mamba_status_string")
+EXPORTED = ("mamba_conv1d_silu", "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd_workspace_bytes",
+            "mamba_scan_fwd", "mamba_scan_step", "mamba_status_string")
 
 
 class MambaDims(ctypes.Structure):
@@ -55,6 +55,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), i32, vp, vp, vp]
     lib.mamba_scan_step.restype = i32
     lib.mamba_scan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), vp, vp]
+    lib.mamba_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.mamba_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(MambaDims), i32]
+    lib.mamba_scan_bwd.restype = i32
+    lib.mamba_scan_bwd.argtypes = [vp] * 9 + [ctypes.POINTER(MambaDims), i32] + [vp] * 9 + [vp]
     lib.mamba_conv1d_silu.restype = i32
     lib.mamba_conv1d_silu.argtypes = [vp, vp, vp, ctypes.POINTER(MambaDims), i32, i32, vp, vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
@@ -108,6 +112,13 @@ def workspace_bytes(dims: MambaDims, dir_mode: int) -> int:
     n = load_library().mamba_scan_fwd_workspace_bytes(ctypes.byref(dims), int(dir_mode))
     if n == ctypes.c_size_t(-1).value:
         raise MambaError(MAMBA_ERR_INVALID, "mamba_scan_fwd_workspace_bytes")
+    return n
+
+
+def bwd_workspace_bytes(dims: MambaDims, dir_mode: int) -> int:
+    n = load_library().mamba_scan_bwd_workspace_bytes(ctypes.byref(dims), int(dir_mode))
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(MAMBA_ERR_UNSUPPORTED, "mamba_scan_bwd_workspace_bytes")
     return n
 
 
@@ -171,6 +182,55 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
     if rc != MAMBA_OK:
         raise MambaError(rc, "mamba_scan_fwd")
     return out, last_state
+
+
+def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dout, dir_mode=DIR_FWD, height=0, width=0,
+             delta_softplus=True, exact_zoh=False, initial_state=None, want_dinit=True, workspace=None,
+             stream=None):
+    """mamba_scan_bwd on torch tensors: gradients of sum(dout * out) for the
+    scan_fwd call with the same arguments.  Returns a dict with du, ddelta,
+    dA, dB, dC (shaped like their inputs), dD and ddelta_bias (None when D or
+    delta_bias is None), dz (None without z) and dinit ([B][K][D][N] float32,
+    None unless want_dinit)."""
+    import torch
+    lib = load_library()
+    K = num_dirs(dir_mode)
+    dev = u.device
+    dt = _dtype_code(u)
+    tdt = u.dtype
+    Bsz, L, Dm = delta.shape[0], delta.shape[-2], delta.shape[-1]
+    N = B.shape[-1]
+    kx = () if K == 1 else (K,)
+    ux = () if (K == 1 or dir_mode == DIR_CROSS2D) else (K,)
+    _check(u, "u", (Bsz,) + ux + (L, Dm), tdt, dev)
+    _check(delta, "delta", (Bsz,) + kx + (L, Dm), tdt, dev)
+    _check(B, "B", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(C, "C", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(z, "z", (Bsz, L, Dm), tdt, dev)
+    _check(dout, "dout", (Bsz, L, Dm), tdt, dev)
+    _check(A, "A", kx + (Dm, N), torch.float32, dev)
+    _check(D, "D", kx + (Dm,), torch.float32, dev)
+    _check(delta_bias, "delta_bias", kx + (Dm,), torch.float32, dev)
+    _check(initial_state, "initial_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dA=torch.empty_like(A),
+             dB=torch.empty_like(B), dC=torch.empty_like(C),
+             dD=None if D is None else torch.empty_like(D), dz=None if z is None else torch.empty_like(z),
+             ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
+             dinit=torch.empty((Bsz,) + kx + (Dm, N), dtype=torch.float32, device=dev) if want_dinit else None)
+    dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
+                     exact_zoh=exact_zoh, initial_state=initial_state)
+    need = bwd_workspace_bytes(dims, dir_mode)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    dims.workspace = workspace.data_ptr()
+    dims.workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                            _ptr(dout), ctypes.byref(dims), int(dir_mode), _ptr(g["du"]), _ptr(g["ddelta"]),
+                            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
+                            _ptr(g["ddelta_bias"]), _ptr(g["dinit"]), _stream(stream))
+    if rc != MAMBA_OK:
+        raise MambaError(rc, "mamba_scan_bwd")
+    return g
 
 
 def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=None, *, delta_softplus=True,

@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "libmamba_scan.so")
 HOST = os.path.join(CSRC, "mamba_scan.hip")
 INST = os.path.join(CSRC, "scan_inst.hip")
 SOURCES = [HOST, INST]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("scan_launch.h", "scan_kernels.h", "device_math.h")] + [
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("scan_launch.h", "scan_kernels.h", "scan_bwd.h", "conv_kernels.h",
+                                                  "device_math.h")] + [
     os.path.join(ROOT, "include", "mamba_scan.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # (bf16, exact) flags of the four instantiation units

@@ -43,6 +43,18 @@ __device__ __forceinline__ float zoh_coef(float a, float x, float dt, float inv_
   return __builtin_fabsf(x) < 0.0625f ? dt * series : direct;
 }
 
+// Derivative of c = (e^{ΔA} - 1)/A with respect to A: (Δ·e^{ΔA} - c)/A.  For
+// small |x| = |ΔA| the difference cancels; there the series of
+// c = Δ·Σ_m x^m/(m+1)! differentiated term by term,
+// Δ²·(1/2 + x/3 + x²/8 + x³/30 + x⁴/144), is used (Δ²/2 at A = 0).
+__device__ __forceinline__ float zoh_coef_dA(float a, float x, float dt, float c, float inv_a) {
+  const float direct = (dt * a - c) * inv_a;
+  const float series = __builtin_fmaf(
+      x, __builtin_fmaf(x, __builtin_fmaf(x, __builtin_fmaf(x, 1.0f / 144.0f, 1.0f / 30.0f), 0.125f), 1.0f / 3.0f),
+      0.5f);
+  return __builtin_fabsf(x) < 0.0625f ? dt * dt * series : direct;
+}
+
 // silu(z) = z·sigmoid(z) = z / (1 + e^{-z}); for z -> -inf, e^{-z} -> inf and
 // the reciprocal gives 0.
 __device__ __forceinline__ float silu_f(float z) { return z * rcp(1.0f + ex2(-z * kLog2e)); }

@@ -106,6 +106,70 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 }
 
 
+// Workspace of the backward pass, in this order (each region 256-byte aligned):
+// the forward recompute's time-split carries, the per-direction fp32 output
+// rows, state checkpoints every 32 positions, dy, the per-channel-block
+// partial sums of dB and dC, the per-direction du of the cross scan, and the
+// per-batch partial sums of dA, dD and ddelta_bias.
+constexpr int kBwdBlock = 16;  // channels per workgroup of scan_bwd_kernel
+struct BwdPlan {
+  Plan fwd;
+  int nblk, ntiles;
+  size_t agg, ws_y, ckpt, dy, dB, dC, du, dA, dD, dbias, total;
+};
+
+int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
+  const int rc = make_plan(g, mode, &bp->fwd);
+  if (rc != MAMBA_OK) return rc;
+  // one state per thread and 32-position checkpoints (the forward tile)
+  if (g->dstate > 16 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  // the recompute always keeps per-direction fp32 rows (32-bit slice offsets)
+  if (g->seqlen * g->dim * 4 > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  const Plan& pl = bp->fwd;
+  const int64_t K = pl.K, Bz = g->batch, L = g->seqlen, Dm = g->dim, N = g->dstate;
+  bp->nblk = (int)((Dm + kBwdBlock - 1) / kBwdBlock);
+  bp->ntiles = (int)((L + kTile - 1) / kTile);
+  if ((int64_t)bp->nblk * Bz * K > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t f4 = sizeof(float);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up(bytes);
+    return at;
+  };
+  bp->agg = take(pl.agg_state_bytes + pl.agg_dsum_bytes);
+  bp->ws_y = take((size_t)K * Bz * L * Dm * f4);
+  bp->ckpt = take((size_t)K * Bz * bp->ntiles * Dm * N * f4);
+  bp->dy = take((size_t)Bz * L * Dm * f4);
+  bp->dB = take((size_t)bp->nblk * Bz * K * L * N * f4);
+  bp->dC = take((size_t)bp->nblk * Bz * K * L * N * f4);
+  bp->du = pl.Ku != K ? take((size_t)K * Bz * L * Dm * f4) : off;
+  bp->dA = take((size_t)Bz * K * Dm * N * f4);
+  bp->dD = take((size_t)Bz * K * Dm * f4);
+  bp->dbias = take((size_t)Bz * K * Dm * f4);
+  bp->total = off;
+  return MAMBA_OK;
+}
+
+template <typename TIn>
+int launch_bwd_prep(const float* ws_y, const void* z, const void* dout, float* dy, void* dz, int K, int64_t n,
+                    hipStream_t stream) {
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL((bwd_prep_kernel<TIn>), dim3(blocks), dim3(256), 0, stream, ws_y, static_cast<const TIn*>(z),
+                     static_cast<const TIn*>(dout), dy, static_cast<TIn*>(dz), K, n);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TOut>
+int launch_bwd_sum(const float* in, int64_t nslices, int64_t stride, int64_t n, void* out, hipStream_t stream) {
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL((bwd_sum_kernel<TOut>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
+                     static_cast<TOut*>(out));
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+
 #ifndef MSCAN_CONV_RUN
 #define MSCAN_CONV_RUN 16
 #endif
@@ -190,6 +254,130 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                : dispatch_scan_f32_simple(dims->dstate, p, pl, stream);
 }
 
+size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_mode) {
+  BwdPlan bp;
+  if (make_bwd_plan(dims, dir_mode, &bp) != MAMBA_OK) return (size_t)-1;
+  return bp.total;
+}
+
+int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const void* dout,
+                   const mamba_dims* dims, int dir_mode, void* du, void* ddelta, float* dA, void* dB, void* dC,
+                   float* dD, void* dz, float* ddelta_bias, float* dinit, hipStream_t stream) {
+  BwdPlan bp;
+  int rc = make_bwd_plan(dims, dir_mode, &bp);
+  if (rc != MAMBA_OK) return rc;
+  if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC) return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD, dz,
+                        ddelta_bias, dinit, dims->initial_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
+  if (!dims->workspace || dims->workspace_bytes < bp.total || !aligned16(dims->workspace))
+    return MAMBA_ERR_WORKSPACE;
+  const Plan& pl = bp.fwd;
+  char* ws = static_cast<char*>(dims->workspace);
+  auto wsf = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const bool bf16 = dims->dtype == MAMBA_DTYPE_BF16;
+  const bool exact = dims->exact_zoh != 0;
+  const int64_t N = dims->dstate;
+
+  // 1. forward recompute: per-direction output rows and state checkpoints
+  ScanParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.delta_bias = delta_bias;
+  p.init_state = dims->initial_state;
+  p.out = nullptr;
+  p.ws_y = wsf(bp.ws_y);
+  p.agg_state = pl.agg_state_bytes ? wsf(bp.agg) : nullptr;
+  p.agg_dsum = pl.agg_dsum_bytes ? wsf(bp.agg + pl.agg_state_bytes) : nullptr;
+  p.last_state = nullptr;
+  p.ckpt = wsf(bp.ckpt);
+  p.ckpt_tiles = bp.ntiles;
+  p.Bsz = (int)dims->batch;
+  p.Dm = (int)dims->dim;
+  p.L = (int)dims->seqlen;
+  p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
+  p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
+  p.K = pl.K;
+  p.Ku = pl.Ku;
+  p.kinds = kinds_of(dir_mode);
+  p.nchunks = pl.nchunks;
+  p.chunk_len = pl.chunk_len;
+  p.nblk_d = pl.nblk_d;
+  p.softplus = dims->delta_softplus ? 1 : 0;
+  rc = bf16 ? (exact ? dispatch_scan_bf16_exact(N, p, pl, stream) : dispatch_scan_bf16_simple(N, p, pl, stream))
+            : (exact ? dispatch_scan_f32_exact(N, p, pl, stream) : dispatch_scan_f32_simple(N, p, pl, stream));
+  if (rc != MAMBA_OK) return rc;
+
+  // 2. dy = dout·silu(z) and dz
+  const int64_t nrow = dims->batch * dims->seqlen * dims->dim;
+  void* dz_out = z ? dz : nullptr;
+  rc = bf16 ? launch_bwd_prep<uint16_t>(p.ws_y, z, dout, wsf(bp.dy), dz_out, pl.K, nrow, stream)
+            : launch_bwd_prep<float>(p.ws_y, z, dout, wsf(bp.dy), dz_out, pl.K, nrow, stream);
+  if (rc != MAMBA_OK) return rc;
+
+  // 3. the reverse sweep
+  BwdParams q{};
+  q.u = u;
+  q.delta = delta;
+  q.A = A;
+  q.B = B;
+  q.C = C;
+  q.D = D;
+  q.delta_bias = delta_bias;
+  q.ckpt = p.ckpt;
+  q.dy = wsf(bp.dy);
+  const bool shared_u = pl.Ku != pl.K;
+  q.du = shared_u ? nullptr : du;
+  q.du_part = shared_u ? wsf(bp.du) : nullptr;
+  q.ddelta = ddelta;
+  q.dB_part = wsf(bp.dB);
+  q.dC_part = wsf(bp.dC);
+  q.dA_part = wsf(bp.dA);
+  q.dD_part = wsf(bp.dD);
+  q.dbias_part = wsf(bp.dbias);
+  q.dinit = dinit;
+  q.Bsz = p.Bsz;
+  q.Dm = p.Dm;
+  q.L = p.L;
+  q.H = p.H;
+  q.W = p.W;
+  q.K = p.K;
+  q.Ku = p.Ku;
+  q.kinds = p.kinds;
+  q.nblk_d = bp.nblk;
+  q.ntiles = bp.ntiles;
+  q.softplus = p.softplus;
+  rc = bf16 ? (exact ? dispatch_bwd_bf16_exact(N, q, stream) : dispatch_bwd_bf16_simple(N, q, stream))
+            : (exact ? dispatch_bwd_f32_exact(N, q, stream) : dispatch_bwd_f32_simple(N, q, stream));
+  if (rc != MAMBA_OK) return rc;
+
+  // 4. sums over channel blocks (dB, dC), directions (du of the cross scan)
+  // and batches (dA, dD, ddelta_bias)
+  const int64_t K = pl.K, Bz = dims->batch, Dm = dims->dim;
+  const int64_t nbc = Bz * K * dims->seqlen * N;
+  if (bf16) {
+    rc = launch_bwd_sum<uint16_t>(q.dB_part, bp.nblk, nbc, nbc, dB, stream);
+    if (rc == MAMBA_OK) rc = launch_bwd_sum<uint16_t>(q.dC_part, bp.nblk, nbc, nbc, dC, stream);
+    if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<uint16_t>(q.du_part, K, nrow, nrow, du, stream);
+  } else {
+    rc = launch_bwd_sum<float>(q.dB_part, bp.nblk, nbc, nbc, dB, stream);
+    if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dC_part, bp.nblk, nbc, nbc, dC, stream);
+    if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<float>(q.du_part, K, nrow, nrow, du, stream);
+  }
+  if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dA_part, Bz, K * Dm * N, K * Dm * N, dA, stream);
+  if (rc == MAMBA_OK && dD) rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream);
+  if (rc == MAMBA_OK && ddelta_bias)
+    rc = launch_bwd_sum<float>(q.dbias_part, Bz, K * Dm, K * Dm, ddelta_bias, stream);
+  return rc;
+}
+
 int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const float* A, const void* B_t,
                     const void* C_t, const float* D, const void* z_t, const float* delta_bias,
                     const mamba_dims* dims, void* out, hipStream_t stream) {
@@ -231,7 +419,7 @@ const char* mamba_status_string(int status) {
     case MAMBA_OK: return "ok";
     case MAMBA_ERR_INVALID: return "invalid argument (null pointer, non-positive size, L != H*W, or unknown mode/dtype)";
     case MAMBA_ERR_UNSUPPORTED: return "unsupported (state size, channel count, alignment or size limit)";
-    case MAMBA_ERR_WORKSPACE: return "workspace missing or smaller than mamba_scan_fwd_workspace_bytes()";
+    case MAMBA_ERR_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() figure";
     case MAMBA_ERR_HIP: return "HIP runtime rejected a kernel launch";
     default: return "unknown status";
   }

@@ -35,4 +35,8 @@ int MSCAN_NAME(dispatch_step, MSCAN_T_NAME, MSCAN_R_NAME)(int64_t N, const StepP
   return dispatch_step<MSCAN_TIN, MSCAN_INST_EXACT != 0>(N, p, s);
 }
 
+int MSCAN_NAME(dispatch_bwd, MSCAN_T_NAME, MSCAN_R_NAME)(int64_t N, const BwdParams& p, hipStream_t s) {
+  return dispatch_bwd<MSCAN_TIN, MSCAN_INST_EXACT != 0>(N, p, s);
+}
+
 }  // namespace mscan

@@ -64,6 +64,7 @@ struct ScanParams {
   float* last_state;        // [Bsz][K][D][N] or null
   float* agg_state;         // [K][Bsz][nchunks-1][D][N]
   float* agg_dsum;          // [K][Bsz][nchunks-1][D]
+  float* ckpt;              // [K][Bsz][ckpt_tiles][D][N] state at every tile start, or null
   int Bsz, Dm, L, H, W;
   int K, Ku;
   int kinds;                // 4 x 2-bit traversal kind, direction k at bits 2k..2k+1
@@ -72,6 +73,7 @@ struct ScanParams {
   int grid_chunks;          // chunks covered by this launch's grid
   int nblk_d;               // channel blocks of 64
   int softplus;
+  int ckpt_tiles;           // tiles of TT positions per sequence (checkpoint rows)
 };
 // Template flag EXACT of the kernels below: exact zero-order-hold input term
 // ((e^{ΔA} - 1)/A)·B·u instead of Δ·B·u [MFS §6.2 Step 4, eq (4)].
@@ -291,6 +293,12 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   float dsum = 0.f;
   // one tile: barrier, scan, barrier, epilogue (the next tile is staged by the caller)
   auto process_tile = [&](int p0) {
+    if (!AGG && p.ckpt && dvalid) {
+      // the state before tile p0, for the recomputation of the backward pass
+      float* S = p.ckpt + ((((int64_t)k * p.Bsz + b) * p.ckpt_tiles + p0 / TT) * D + d) * N + ng * G;
+#pragma unroll
+      for (int j = 0; j < G; ++j) S[j] = h[j];
+    }
     __syncthreads();
     const int tlen = min(TT, pend - p0);
     // Rows of the tile past the chunk end were staged as Δ' = 0, Δu = 0, B = C = 0:

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "../../include/mamba_scan.h"
+#include "scan_bwd.h"
 #include "scan_kernels.h"
 
 namespace mscan {
@@ -61,7 +62,8 @@ struct Plan {
 // zero-order hold or Δ·B·u).
 #define MSCAN_DECLARE_DISPATCH(SUFFIX)                                                        \
   int dispatch_scan_##SUFFIX(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s); \
-  int dispatch_step_##SUFFIX(int64_t N, const StepParams& p, hipStream_t s);
+  int dispatch_step_##SUFFIX(int64_t N, const StepParams& p, hipStream_t s);              \
+  int dispatch_bwd_##SUFFIX(int64_t N, const BwdParams& p, hipStream_t s);
 MSCAN_DECLARE_DISPATCH(bf16_simple)
 MSCAN_DECLARE_DISPATCH(bf16_exact)
 MSCAN_DECLARE_DISPATCH(f32_simple)
@@ -96,7 +98,7 @@ int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
     rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
   }
   if (rc != MAMBA_OK) return rc;
-  if (p.ws_y) {
+  if (p.ws_y && p.out) {  // (the backward pass keeps only the per-direction rows)
     const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
     const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
     hipLaunchKernelGGL((merge_dirs_kernel<TIn>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
@@ -138,6 +140,26 @@ int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
     case 16: return launch_step<TIn, 16, EXACT>(p, s);
     case 32: return launch_step<TIn, 32, EXACT>(p, s);
     case 64: return launch_step<TIn, 64, EXACT>(p, s);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+
+template <typename TIn, int N, bool EXACT>
+int launch_bwd(const BwdParams& p, hipStream_t stream) {
+  constexpr int NT = 16 * (N < 4 ? 4 : N);
+  const unsigned blocks = (unsigned)(p.nblk_d * p.Bsz * p.K);
+  hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TIn, bool EXACT>
+int dispatch_bwd(int64_t N, const BwdParams& p, hipStream_t s) {
+  switch (N) {
+    case 1: return launch_bwd<TIn, 1, EXACT>(p, s);
+    case 2: return launch_bwd<TIn, 2, EXACT>(p, s);
+    case 4: return launch_bwd<TIn, 4, EXACT>(p, s);
+    case 8: return launch_bwd<TIn, 8, EXACT>(p, s);
+    case 16: return launch_bwd<TIn, 16, EXACT>(p, s);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }

@@ -129,3 +129,11 @@ def make_conv_inputs(batch: int, seqlen: int, dim: int, width: int, dtype: str, 
     weight = rng.uniform(-bound, bound, size=(dim, width)).astype(np.float32)
     bias = rng.uniform(-bound, bound, size=dim).astype(np.float32)
     return dict(x=x, weight=weight, bias=bias)
+
+
+def make_dout(w: Workload, seqlen: int | None = None) -> np.ndarray:
+    """Upstream gradient dout [B][L][D] of the backward pass: standard normal,
+    rounded to bf16 for bf16 workloads, from its own stream of the workload's seed."""
+    L = w.seqlen if seqlen is None else seqlen
+    rng = np.random.Generator(np.random.PCG64([w.seed, 2]))
+    return _normal(rng, (w.batch, L, w.dim), w.dtype)

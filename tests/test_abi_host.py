@@ -133,3 +133,34 @@ def test_conv1d_validation(lib):
     assert conv(dims(dim=60)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert conv(d, x=FAKE + 8) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert conv(d, w=FAKE + 2) == ms._binding.MAMBA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_and_validation(lib):
+    d = dims()
+    need = ms.bwd_workspace_bytes(d, ms.DIR_FWD)
+    # at least: per-direction fp32 rows, dy, 32-step checkpoints, dB/dC partials per 16-channel block
+    L, Dm, N, Bz = 100, 64, 16, 2
+    assert need >= 4 * (Bz * L * Dm * 2 + Bz * 4 * Dm * N + 2 * (Dm // 16) * Bz * L * N)
+    assert need % 256 == 0 and ms.bwd_workspace_bytes(d, ms.DIR_FWD) == need
+    cross = ms.bwd_workspace_bytes(dims(seqlen=96, height=8, width=12), ms.DIR_CROSS2D)
+    assert cross >= 4 * 4 * Bz * 96 * Dm * 2  # per-direction rows and per-direction du
+    for bad in (dims(dstate=32), dims(dstate=64), dims(seqlen=0), dims(dim=60)):
+        with pytest.raises(ms.MambaError):
+            ms.bwd_workspace_bytes(bad, ms.DIR_FWD)
+
+    def bwd(dd, mode=ms.DIR_FWD, **ptrs):
+        p = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, dout=FAKE, du=FAKE,
+                 ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dinit=None)
+        p.update(ptrs)
+        return lib.mamba_scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"], p["dout"],
+                                  ctypes.byref(dd), mode, p["du"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
+                                  p["dz"], p["dbias"], p["dinit"], None)
+    E = ms._binding
+    assert bwd(d, dout=None) == E.MAMBA_ERR_INVALID
+    assert bwd(d, dB=None) == E.MAMBA_ERR_INVALID
+    assert bwd(dims(batch=0)) == E.MAMBA_ERR_INVALID
+    assert bwd(d, mode=7) == E.MAMBA_ERR_INVALID
+    assert bwd(dims(dstate=32)) == E.MAMBA_ERR_UNSUPPORTED
+    assert bwd(d, dz=FAKE + 2) == E.MAMBA_ERR_UNSUPPORTED
+    assert bwd(d) == E.MAMBA_ERR_WORKSPACE  # the backward pass always needs its workspace
+    assert bwd(dims(workspace=FAKE, workspace_bytes=need - 256)) == E.MAMBA_ERR_WORKSPACE
