@@ -10,7 +10,8 @@ four fp32 operations), so the bound reported is "alu" in elements/s, with the
 HBM view alongside.  `cpu_baseline` times the fp64 CPU oracle on a bounded
 sample of the same workload.  `conv1d` times the causal depthwise Conv1d + SiLU
 prologue on the layer's activations against the HBM peak (it is bandwidth
-bound).
+bound).  `backward` times mamba_scan_bwd (the gradients of every input) on the
+same workload against its vector-ALU floor.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-cpu-baseline] [--decode-steps S]
@@ -41,6 +42,20 @@ FP32_LANE_OPS = 256 * 4 * 32 * 2.4e9
 EXP_LANE_OPS = FP32_LANE_OPS / 4
 ALU_PEAK_ELEM = 1.0 / (4.0 / FP32_LANE_OPS + 1.0 / EXP_LANE_OPS)
 HBM_PEAK_GBS = 8000.0
+# Backward pass, per element: two exps (the forward recompute that writes the
+# checkpoints, and the segment recompute) and 21 fp32 operations (4 in each
+# recompute; 13 in the adjoint step: λ, the dΔ, dA, dB, du terms, dC, the carry).
+BWD_ALU_PEAK_ELEM = 1.0 / (21.0 / FP32_LANE_OPS + 2.0 / EXP_LANE_OPS)
+
+
+def bwd_algorithmic_bytes(w) -> int:
+    """Inputs (and dout) read once, every gradient written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    K, Bsz, L, Dm, N = w.ndirs, w.batch, w.seqlen, w.dim, w.dstate
+    Ku = 1 if w.dir_mode == 3 else K
+    act = 2 * (Bsz * Ku * L * Dm + Bsz * K * L * Dm + (Bsz * L * Dm if w.gated else 0)) * e  # u, delta, z and grads
+    bc = 2 * 2 * Bsz * K * L * N * e                                                        # B, C and grads
+    return act + bc + Bsz * L * Dm * e + 2 * (K * Dm * N * 4 + 2 * K * Dm * 4)             # dout; A, D, bias, grads
 
 
 def algorithmic_bytes(w) -> int:
@@ -128,6 +143,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--conv-steps", type=int, default=20, help="timed calls of the Conv1d + SiLU prologue (0: skip)")
+    ap.add_argument("--bwd-steps", type=int, default=10, help="timed calls of the backward pass (0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one torch elementwise kernel that reads and writes a "
                          "MIB-MiB buffer (known bytes, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -250,6 +266,36 @@ def main():
                 "us_per_call": conv_s * 1e6, "algorithmic_bytes": cbytes, "achieved_gbs": cbytes / conv_s / 1e9,
                 "peak_gbs": HBM_PEAK_GBS, "frac": cbytes / conv_s / 1e9 / HBM_PEAK_GBS, "bound": "hbm"}
 
+    bwd = None
+    if args.bwd_steps > 0 and w.dstate <= 16:
+        douts = [todev(I.make_dout(w.with_(seed=w.seed + 1000 * s_))) for s_ in range(len(sets))]
+        bws = torch.empty(ms.bwd_workspace_bytes(dims, w.dir_mode), dtype=torch.uint8, device=dev)
+
+        def bstep(i):
+            s_ = sets[i % len(sets)]
+            return ms.scan_bwd(s_["u"], s_["delta"], s_["A"], s_["B"], s_["C"], s_["D"], s_["z"], s_["delta_bias"],
+                               dout=douts[i % len(sets)], dir_mode=w.dir_mode, height=w.height, width=w.width,
+                               workspace=bws, stream=stream)
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                bstep(i)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.bwd_steps)]
+            for i in range(args.bwd_steps):
+                evs[i][0].record(stream)
+                bstep(i)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+        bwd_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        bbytes = bwd_algorithmic_bytes(w)
+        bwd = {"op": "mamba_scan_bwd: gradients of u, delta, A, B, C, D, z, delta_bias, initial state",
+               "us_per_call": bwd_s * 1e6, "elements_per_s": el / bwd_s, "bound": "alu",
+               "peak_elements_per_s": BWD_ALU_PEAK_ELEM, "frac": el / bwd_s / BWD_ALU_PEAK_ELEM,
+               "algorithmic_bytes": bbytes, "hbm_gbs": bbytes / bwd_s / 1e9,
+               "workspace_bytes": int(bws.numel())}
+        del bws, douts
+
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -285,6 +331,7 @@ def main():
         "cpu_baseline": cpu,
         "decode": decode,
         "conv1d": conv,
+        "backward": bwd,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)

@@ -155,17 +155,24 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
 template <typename TIn>
 int launch_bwd_prep(const float* ws_y, const void* z, const void* dout, float* dy, void* dz, int K, int64_t n,
                     hipStream_t stream) {
-  const unsigned blocks = (unsigned)((n + 255) / 256);
+  const unsigned blocks = (unsigned)((n / 8 + 255) / 256);
   hipLaunchKernelGGL((bwd_prep_kernel<TIn>), dim3(blocks), dim3(256), 0, stream, ws_y, static_cast<const TIn*>(z),
                      static_cast<const TIn*>(dout), dy, static_cast<TIn*>(dz), K, n);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
+// (stride == n at every call: the partial slices are packed)
 template <typename TOut>
 int launch_bwd_sum(const float* in, int64_t nslices, int64_t stride, int64_t n, void* out, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL((bwd_sum_kernel<TOut>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
-                     static_cast<TOut*>(out));
+  if (n % 4 == 0 && stride % 4 == 0) {
+    const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
+    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 4>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
+                       static_cast<TOut*>(out));
+  } else {
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 1>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
+                       static_cast<TOut*>(out));
+  }
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

@@ -29,6 +29,13 @@
 
 namespace mscan {
 
+#ifndef MSCAN_BWD_WAVES
+#define MSCAN_BWD_WAVES 2  // waves per SIMD the adjoint kernel's register budget is sized for (3 spills)
+#endif
+#ifndef MSCAN_BWD_KEEP_ABAR
+#define MSCAN_BWD_KEEP_ABAR 1  // 1: keep the segment's e^{ΔA} from the recompute (32 registers) instead of recomputing
+#endif
+
 // ---- row butterfly (16 lanes of a row hold the 16 channels of one state) ----
 __device__ __forceinline__ float bwd_quad_perm_xor2(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4e, 0xf, 0xf, false));
@@ -58,26 +65,6 @@ __device__ __forceinline__ float bwd_bfly4(float x, float y) {
       : "v"(x), "v"(y));
   return r;
 }
-// v[s] (s = 0..15) per lane; returns, in lane j of each 16-lane row, the sum
-// over the row's lanes of v[j].
-__device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], int j) {
-  float r8[8], r4[4], r2[2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r8[i] = bwd_bfly8(v[i], v[i + 8]);    // step i + 8*bit3(j)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r4[i] = bwd_bfly4(r8[i], r8[i + 4]);  // + 4*bit2(j)
-  const bool b1 = (j & 2) != 0, b0 = (j & 1) != 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float send = b1 ? r4[i] : r4[i + 2];
-    const float keep = b1 ? r4[i + 2] : r4[i];
-    r2[i] = keep + bwd_quad_perm_xor2(send);
-  }
-  const float send = b0 ? r2[0] : r2[1];
-  const float keep = b0 ? r2[1] : r2[0];
-  return keep + bwd_quad_perm_xor1(send);  // step j
-}
-
 struct BwdParams {
   const void* u;
   const void* delta;
@@ -101,43 +88,97 @@ struct BwdParams {
 };
 
 // dy = dout·silu(z), dz = dout·y_all·silu'(z) with y_all = Σ_k y_k (ungated);
-// without a gate dy = dout.  One thread per element.
+// without a gate dy = dout.  Eight consecutive elements per thread (n is a
+// multiple of 8: the channel count is).
 template <typename TIn>
 __global__ void __launch_bounds__(256) bwd_prep_kernel(const float* __restrict__ ws_y, const TIn* __restrict__ z,
                                                        const TIn* __restrict__ dout, float* __restrict__ dy,
                                                        TIn* __restrict__ dz, int K, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= n) return;
-  const float go = to_f32(load1(dout + i));
+  Vec<TIn, 8> go;
+  go.load(dout + i);
+  float d8[8];
   if (z == nullptr) {
-    dy[i] = go;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) d8[c] = go.get(c);
+    storeV<8>(dy + i, d8);
     return;
   }
-  float y = 0.f;
-  if (dz)
-    for (int k = 0; k < K; ++k) y += ws_y[k * n + i];
-  const float zz = to_f32(load1(z + i));
-  const float sg = rcp(1.0f + ex2(-zz * kLog2e));
-  dy[i] = go * zz * sg;
-  if (dz) store1(dz + i, go * y * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
+  Vec<TIn, 8> zv;
+  zv.load(z + i);
+  float y8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (dz) {
+    for (int k = 0; k < K; ++k) {
+      Vec<float, 8> yk;
+      yk.load(ws_y + k * n + i);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y8[c] += yk.get(c);
+    }
+  }
+  float g8[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float zz = zv.get(c), g = go.get(c);
+    const float sg = rcp(1.0f + ex2(-zz * kLog2e));
+    d8[c] = g * zz * sg;
+    g8[c] = g * y8[c] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+  }
+  storeV<8>(dy + i, d8);
+  if (dz) storeV<8>(dz + i, g8);
 }
 
-// out[i] = Σ_s in[s·stride + i], s = 0 .. nslices-1 in order.
-template <typename TOut>
+// out[i] = Σ_s in[s·stride + i], s = 0 .. nslices-1 in order; V consecutive
+// elements per thread (V = 4 needs n and stride multiples of 4).
+template <typename TOut, int V>
 __global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ in, int64_t nslices, int64_t stride,
                                                       int64_t n, TOut* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= n) return;
-  float acc = 0.f;
-  for (int64_t s = 0; s < nslices; ++s) acc += in[s * stride + i];
-  store1(out + i, acc);
+  if constexpr (V == 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t s = 0; s < nslices; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(in + s * stride + i);
+      acc[0] += v.x;
+      acc[1] += v.y;
+      acc[2] += v.z;
+      acc[3] += v.w;
+    }
+    storeV<4>(out + i, acc);
+  } else {
+    float acc = 0.f;
+    for (int64_t s = 0; s < nslices; ++s) acc += in[s * stride + i];
+    store1(out + i, acc);
+  }
+}
+
+// Lane-mask select: m all ones gives x, all zeros gives y (one v_bfi_b32).
+__device__ __forceinline__ float bsel(uint32_t m, float x, float y) {
+  return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(y) & ~m));
+}
+
+// v[s] (s = 0..15) per lane; returns, in lane j of each 16-lane row, the sum
+// over the row's lanes of v[j].  m1, m0: all-ones masks of bit 1 and bit 0 of j.
+__device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint32_t m1, uint32_t m0) {
+  float r8[8], r4[4], r2[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r8[i] = bwd_bfly8(v[i], v[i + 8]);    // step i + 8*bit3(j)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r4[i] = bwd_bfly4(r8[i], r8[i + 4]);  // + 4*bit2(j)
+#pragma unroll
+  for (int i = 0; i < 2; ++i)  // + 2*bit1(j): keep that half, send the other to lane j^2
+    r2[i] = bsel(m1, r4[i + 2], r4[i]) + bwd_quad_perm_xor2(bsel(m1, r4[i], r4[i + 2]));
+  return bsel(m0, r2[1], r2[0]) + bwd_quad_perm_xor1(bsel(m0, r2[0], r2[1]));  // step j
 }
 
 // One workgroup: 16 channels of one (direction, batch) for the whole
 // sequence, walked backwards.  Thread tid: channel cl = tid % 16, state
-// n = tid / 16 (rows n >= N only pad small N to a whole wave).
+// n = tid / 16 (rows n >= N only pad small N to a whole wave).  The global
+// loads of the next (earlier) segment are issued before the current one is
+// computed, and the staged rows hold Δ in natural units (the exp takes
+// A·log2 e).
 template <typename TIn, int N, bool EXACT>
-__global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
   constexpr int NGP = N < 4 ? 4 : N;  // thread rows
   constexpr int NT = CB * NGP;
@@ -147,23 +188,26 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
   constexpr int TPH = TH / NGP > 0 ? TH / NGP : 1;  // positions summed per thread per half
   constexpr int PS = TS + 4;          // padded row of a per-channel or per-state array
   constexpr int YS = TH + 4;          // padded partial row
+  constexpr int QI = (N * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment
   static_assert(TS % NGP == 0 && TH % 4 == 0, "segment splits over the thread rows");
   static_assert(N <= 16, "one state per thread");
 
-  __shared__ __attribute__((aligned(16))) float s_dl[CB * PS];   // Δ' = Δ·log2 e
+  __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ
   __shared__ __attribute__((aligned(16))) float s_u[CB * PS];    // u
   __shared__ __attribute__((aligned(16))) float s_dy[CB * PS];   // dy
   __shared__ __attribute__((aligned(16))) float s_B[N * PS];
   __shared__ __attribute__((aligned(16))) float s_C[N * PS];
   __shared__ __attribute__((aligned(16))) float s_pd[N][CB][YS];  // per-state parts of dΔ
   __shared__ __attribute__((aligned(16))) float s_pu[N][CB][YS];  // per-state parts of du
-  __shared__ float s_red[2][NGP][CB];
+  // (the final per-channel sums reuse s_pd: 2·NGP·CB floats, after the last barrier)
+  static_assert(2 * NGP <= N * YS, "room for the final sums");
 
   const int tid = threadIdx.x;
   const int cl = tid % CB;
   const int ng = tid / CB;
   const bool nvalid = ng < N;
   const int n = nvalid ? ng : 0;
+  const uint32_t m1 = (cl & 2) ? ~0u : 0u, m0 = (cl & 1) ? ~0u : 0u;
 
   const int nblocks = gridDim.x;
   int bid = logical_block(blockIdx.x, nblocks, 4);
@@ -190,60 +234,92 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
   const TIn* B_s = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* C_s = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
   const float* dy_s = p.dy + (int64_t)b * L * D;
+  const float* ck_s = p.ckpt + ((int64_t)k * p.Bsz + b) * p.ntiles * D * N;
+  const bool own = nvalid && dvalid;  // this thread's (channel, state) exists
+  const int64_t ck_off = own ? (int64_t)d * N + n : 0;
 
-  const float Anat = (nvalid && dvalid) ? p.A[((int64_t)k * D + d) * N + n] : 0.f;
+  const float Anat = own ? p.A[((int64_t)k * D + d) * N + n] : 0.f;
+  const float Al2 = Anat * kLog2e;  // e^{ΔA} = 2^{Δ·A·log2 e}
   const float invA = Anat != 0.f ? 1.0f / Anat : 0.f;
   const float bias = (dvalid && p.delta_bias) ? p.delta_bias[k * D + d] : 0.f;
   const float Dd = (dvalid && p.D) ? p.D[k * D + d] : 0.f;
 
+  // raw global values of one segment (rows clamped into the sequence; padded
+  // rows are zeroed at staging)
+  struct Raw {
+    TIn dl[TPS], u[TPS], B[QI], C[QI];
+    float dy[TPS], h0;
+  };
+  auto load_seg = [&](int seg, Raw& r) __attribute__((always_inline)) {
+    const int p0 = seg * TS;
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+      const int64_t off = (int64_t)token(min(p0 + ng * TPS + i, L - 1)) * D + dc;
+      r.dl[i] = dl_s[off];
+      r.u[i] = u_s[off];
+      r.dy[i] = dy_s[off];
+    }
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      const int q = min(tid + i * NT, N * TS - 1);
+      const int64_t off = (int64_t)token(min(p0 + q / N, L - 1)) * N + q % N;
+      r.B[i] = B_s[off];
+      r.C[i] = C_s[off];
+    }
+    r.h0 = ck_s[(int64_t)seg * D * N + ck_off];
+  };
+  auto stage_seg = [&](int seg, const Raw& r) __attribute__((always_inline)) {
+    const int p0 = seg * TS;
+#pragma unroll
+    for (int i = 0; i < TPS; ++i) {
+      const int tt = ng * TPS + i;
+      const float okf = (p0 + tt < L && dvalid) ? 1.f : 0.f;
+      const float x = to_f32(r.dl[i]) + bias;
+      s_dt[cl * PS + tt] = (p.softplus ? softplus_log2(x) * kLn2 : x) * okf;
+      s_u[cl * PS + tt] = to_f32(r.u[i]) * okf;
+      s_dy[cl * PS + tt] = r.dy[i] * okf;
+    }
+#pragma unroll
+    for (int i = 0; i < QI; ++i) {
+      const int q = tid + i * NT;
+      if (QI * NT == N * TS || q < N * TS) {
+        const float okf = p0 + q / N < L ? 1.f : 0.f;
+        s_B[(q % N) * PS + q / N] = to_f32(r.B[i]) * okf;
+        s_C[(q % N) * PS + q / N] = to_f32(r.C[i]) * okf;
+      }
+    }
+  };
+
   float carry = 0.f;  // Ā_{p+1}·λ_{p+1}
   float dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
 
+  Raw raw;
+  load_seg(p.ntiles - 1, raw);
   // (Every read of the staging arrays comes before the last barrier of the
   // previous segment, so staging needs no barrier of its own.)
   for (int seg = p.ntiles - 1; seg >= 0; --seg) {
     const int p0 = seg * TS;
-    // ---- stage the segment: per (position, channel) and per (position, state) ----
-#pragma unroll
-    for (int i = 0; i < TPS; ++i) {
-      const int tt = ng * TPS + i;
-      const int pp = p0 + tt;
-      const float okf = (pp < L && dvalid) ? 1.f : 0.f;
-      const int64_t off = (int64_t)token(min(pp, L - 1)) * D + dc;
-      const float x = to_f32(load1(dl_s + off)) + bias;
-      s_dl[cl * PS + tt] = (p.softplus ? softplus_log2(x) : x * kLog2e) * okf;
-      s_u[cl * PS + tt] = to_f32(load1(u_s + off)) * okf;
-      s_dy[cl * PS + tt] = dy_s[off] * okf;
-    }
-    for (int q = tid; q < N * TS; q += NT) {
-      const int nn = q % N, tt = q / N;
-      const int pp = p0 + tt;
-      const float okf = pp < L ? 1.f : 0.f;
-      const int64_t off = (int64_t)token(min(pp, L - 1)) * N + nn;
-      s_B[nn * PS + tt] = to_f32(load1(B_s + off)) * okf;
-      s_C[nn * PS + tt] = to_f32(load1(C_s + off)) * okf;
-    }
+    stage_seg(seg, raw);
+    const float h0 = own ? raw.h0 : 0.f;
     __syncthreads();
+    if (seg > 0) load_seg(seg - 1, raw);
 
     // ---- recompute the segment's states from its checkpoint ----
-    const float h0 = (nvalid && dvalid) ? p.ckpt[((((int64_t)k * p.Bsz + b) * p.ntiles + seg) * D + d) * N + n] : 0.f;
-    float hs[TS], as[TS];
+    float hs[TS], as[MSCAN_BWD_KEEP_ABAR ? TS : 1];
     {
       float h = h0;
 #pragma unroll
       for (int s = 0; s < TS; ++s) {
-        const float dl = s_dl[cl * PS + s];
+        const float dt = s_dt[cl * PS + s];
         const float uu = s_u[cl * PS + s];
         const float Bv = s_B[n * PS + s];
-        const float a = ex2(dl * Anat);
-        const float dt = dl * kLn2;
+        const float a = ex2(dt * Al2);
         const float c = EXACT ? zoh_coef(a, dt * Anat, dt, invA) : dt;
-        h = __builtin_fmaf(a, h, c * Bv * uu);
+        h = __builtin_fmaf(a, h, c * uu * Bv);
         hs[s] = h;
-        as[s] = a;
+        if constexpr (MSCAN_BWD_KEEP_ABAR) as[s] = a;
       }
     }
-
     // The adjoint reads the staged values again from LDS: kept live from the
     // recompute they would take five registers per position.
     asm volatile("" ::: "memory");
@@ -251,50 +327,57 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
     // ---- the adjoint over the two halves, later half first ----
 #pragma unroll
     for (int half = 1; half >= 0; --half) {
-      float pB[TH], pC[TH];
 #pragma unroll
-      for (int s4 = TH - 4; s4 >= 0; s4 -= 4) {
-        float pd4[4], pu4[4];
+      for (int qt = 1; qt >= 0; --qt) {
+        // dB and dC terms of the quarter's 8 steps: [r] dB of step r, [8 + r] dC
+        float pBC[16];
 #pragma unroll
-        for (int r = 3; r >= 0; --r) {
-          const int s = half * TH + s4 + r;
-          const float dl = s_dl[cl * PS + s];
-          const float uu = s_u[cl * PS + s];
-          const float dyv = s_dy[cl * PS + s];
-          const float Bv = s_B[n * PS + s];
-          const float Cv = s_C[n * PS + s];
-          const float a = as[s];
-          const float hp = s > 0 ? hs[s - 1] : h0;
-          const float dt = dl * kLn2;
-          const float l = __builtin_fmaf(Cv, dyv, carry);
-          const float ga = l * hp;
-          float c = dt, dcdt = 1.f;
-          if constexpr (EXACT) {
-            c = zoh_coef(a, dt * Anat, dt, invA);
-            dcdt = a;  // dc/dΔ = e^{ΔA}
-            dA_acc = __builtin_fmaf(l * zoh_coef_dA(a, dt * Anat, dt, c, invA), Bv * uu, dA_acc);
+        for (int s4 = 4; s4 >= 0; s4 -= 4) {
+          float pd4[4], pu4[4];
+#pragma unroll
+          for (int r = 3; r >= 0; --r) {
+            const int sq = s4 + r;                 // step within the quarter
+            const int s = half * TH + qt * 8 + sq;  // step within the segment
+            const float dt = s_dt[cl * PS + s];
+            const float uu = s_u[cl * PS + s];
+            const float dyv = s_dy[cl * PS + s];
+            const float Bv = s_B[n * PS + s];
+            const float Cv = s_C[n * PS + s];
+            const float a = MSCAN_BWD_KEEP_ABAR ? as[s] : ex2(dt * Al2);
+            const float hp = s > 0 ? hs[s - 1] : h0;
+            const float l = __builtin_fmaf(Cv, dyv, carry);  // λ
+            const float ga = l * hp;
+            const float lB = l * Bv;
+            if constexpr (EXACT) {
+              const float x = dt * Anat;
+              const float c = zoh_coef(a, x, dt, invA);
+              // dc/dΔ = e^{ΔA}; dc/dA from zoh_coef_dA
+              pd4[r] = __builtin_fmaf(ga * Anat, a, a * lB * uu);
+              pu4[r] = lB * c;
+              dA_acc = __builtin_fmaf(lB * zoh_coef_dA(a, x, dt, c, invA), uu, dA_acc);
+              pBC[sq] = l * c * uu;
+            } else {
+              pd4[r] = __builtin_fmaf(ga * Anat, a, lB * uu);
+              pu4[r] = lB * dt;
+              pBC[sq] = l * dt * uu;
+            }
+            dA_acc = __builtin_fmaf(ga * dt, a, dA_acc);
+            pBC[8 + sq] = dyv * hs[s];
+            carry = a * l;
           }
-          pd4[r] = __builtin_fmaf(ga * Anat, a, l * dcdt * Bv * uu);
-          pu4[r] = l * c * Bv;
-          dA_acc = __builtin_fmaf(ga * dt, a, dA_acc);
-          pB[s4 + r] = l * c * uu;
-          pC[s4 + r] = dyv * hs[s];
-          carry = a * l;
+          if (nvalid) {
+            const int sh = qt * 8 + s4;  // position within the half
+            *reinterpret_cast<float4*>(&s_pd[n][cl][sh]) = make_float4(pd4[0], pd4[1], pd4[2], pd4[3]);
+            *reinterpret_cast<float4*>(&s_pu[n][cl][sh]) = make_float4(pu4[0], pu4[1], pu4[2], pu4[3]);
+          }
         }
-        if (nvalid) {
-          *reinterpret_cast<float4*>(&s_pd[n][cl][s4]) = make_float4(pd4[0], pd4[1], pd4[2], pd4[3]);
-          *reinterpret_cast<float4*>(&s_pu[n][cl][s4]) = make_float4(pu4[0], pu4[1], pu4[2], pu4[3]);
-        }
-      }
-      // dB, dC: sums over the row's 16 channels; lane cl ends with step cl
-      const float sB = row_sum_transpose16(pB, cl);
-      const float sC = row_sum_transpose16(pC, cl);
-      {
-        const int pp = p0 + half * TH + cl;
+        // sums over the row's 16 channels: lane cl < 8 ends with dB of step
+        // cl, lane cl >= 8 with dC of step cl - 8
+        const float sBC = row_sum_transpose16(pBC, m1, m0);
+        const int pp = p0 + half * TH + qt * 8 + (cl & 7);
         if (nvalid && pp < L) {
           const int64_t off = ((((int64_t)dblk * p.Bsz + b) * p.K + k) * L + token(pp)) * N + n;
-          p.dB_part[off] = sB;
-          p.dC_part[off] = sC;
+          (cl < 8 ? p.dB_part : p.dC_part)[off] = sBC;
         }
       }
       __syncthreads();
@@ -311,11 +394,11 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
             dd += s_pd[g][cl][sh];
             duu += s_pu[g][cl][sh];
           }
-          const float dl = s_dl[cl * PS + s];
+          const float dt = s_dt[cl * PS + s];
           const float uu = s_u[cl * PS + s];
           const float dyv = s_dy[cl * PS + s];
-          // σ(x) = 1 - e^{-Δ} for Δ = softplus(x)
-          const float dx = p.softplus ? dd * (1.0f - ex2(-dl)) : dd;
+          // softplus'(x) = sigmoid(x) = 1 - e^{-Δ}
+          const float dx = p.softplus ? dd * (1.0f - ex2(-dt * kLog2e)) : dd;
           duu = __builtin_fmaf(Dd, dyv, duu);
           dD_acc = __builtin_fmaf(dyv, uu, dD_acc);
           dbias_acc += dx;
@@ -332,8 +415,9 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
   }
 
   // ---- per-(b, k, d) and per-(b, k, d, n) results ----
-  s_red[0][ng][cl] = dD_acc;
-  s_red[1][ng][cl] = dbias_acc;
+  float* s_red = &s_pd[0][0][0];  // [2][NGP][CB]
+  s_red[ng * CB + cl] = dD_acc;
+  s_red[(NGP + ng) * CB + cl] = dbias_acc;
   __syncthreads();
   if (dvalid) {
     if (nvalid) {
@@ -345,8 +429,8 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N)) scan_bwd_kernel(const Bw
       float sD = 0.f, sb = 0.f;
 #pragma unroll
       for (int g = 0; g < NGP; ++g) {
-        sD += s_red[0][g][cl];
-        sb += s_red[1][g][cl];
+        sD += s_red[g * CB + cl];
+        sb += s_red[(NGP + g) * CB + cl];
       }
       p.dD_part[((int64_t)b * p.K + k) * D + d] = sD;
       p.dbias_part[((int64_t)b * p.K + k) * D + d] = sb;
