@@ -47,6 +47,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError("libmamba_scan.so is not built (%s); run `python -m selective_state_space_mamba_amd.build` "
                            "or __graft_entry__.build()" % path)
+    # torch's wheel bundles its own HIP runtime under the same soname
+    # (libamdhip64.so.7) but asks for it as libamdhip64.so: loaded after torch,
+    # the library binds to torch's runtime (one runtime, shared streams and
+    # memory); loaded first, it would pull in the system runtime and torch a
+    # second one.  So torch is imported first.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
     lib.mamba_scan_fwd_workspace_bytes.restype = ctypes.c_size_t

@@ -27,7 +27,8 @@
 //   * per scan step and state: Ā = 2^(Δ'·A) = exp(Δ·A) (one v_exp_f32),
 //     h = Ā·h + (Δ'u)·(B ln 2), and the partial readout Σ C·h over the
 //     thread's G states [MFS §2.2 eq (2a)(2b); §6.2 Step 4 eq (4); MUN §4];
-//   * the NG partial readouts meet in LDS; the epilogue adds them in order,
+//   * the NG partial readouts meet in LDS (NG/4 with 16-channel blocks, whose
+//     waves first sum their 4 state rows in registers); the epilogue adds them,
 //     adds the D·u skip [MUN §4], applies the silu(z) gate [MFS §6.2 Step 6]
 //     and stores the output row.  With several directions the ungated fp32
 //     row goes to a workspace slice instead and merge_dirs_kernel sums the
@@ -118,7 +119,11 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   __shared__ float s_dd[CB * DS];              // [c][2t] = Δ'_t, [c][2t+1] = Δ_t·u_t
   __shared__ float s_B[N * BS];                // [n][t] = B_t[n]·ln 2
   __shared__ float s_C[AGG ? 4 : N * BS];      // [n][t] = C_t[n]
-  __shared__ float s_y[AGG ? 1 : NG][AGG ? 1 : CB][AGG ? 4 : YS];  // partial readouts, time-contiguous
+  // Partial readouts, time-contiguous.  With 16-channel blocks a wave holds 4
+  // state rows of the same 16 channels; they are summed in registers first
+  // (two cross-lane swap stages), so each output has NG/4 partials.
+  constexpr int NY = CB == 16 ? NG / 4 : NG;
+  __shared__ float s_y[AGG ? 1 : NY][AGG ? 1 : CB][AGG ? 4 : YS];
 
   const int tid = threadIdx.x;
   const int cl = tid % CB;  // channel within the block
@@ -355,7 +360,21 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
           if constexpr (!AGG) y[r] = __builtin_fmaf(o.C[j][r], h[j], y[r]);
         }
       if constexpr (AGG) dsum += (o.dl[0] + o.dl[1]) + (o.dl[2] + o.dl[3]);
-      else *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
+      else if constexpr (CB == 16) {
+        // Steps (0, 2) and (1, 3): swapping lanes 32-63 of one with lanes 0-31
+        // of the other and adding sums the wave's two halves (rows 0+2, 1+3),
+        // steps 0/1 landing in the low half and 2/3 in the high half; the
+        // same with odd/even 16-lane rows then sums rows 0+1 (2+3), leaving
+        // in row r the 4-row sum of step r.
+        const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[0]), __float_as_uint(y[2]), false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[1]), __float_as_uint(y[3]), false, false);
+        const float z02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+        const float z13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+        const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(z02), __float_as_uint(z13), false, false);
+        s_y[ng >> 2][cl][tt + (ng & 3)] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+      } else {
+        *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
+      }
     };
     Ops o0, o1;
     read_ops(o0, 0);
@@ -377,7 +396,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
 #pragma unroll
       for (int i = 0; i < TPT; ++i) yv[i] = Du[i];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
+      for (int g = 0; g < NY; ++g) {
 #pragma unroll
         for (int i = 0; i < TPT; ++i) yv[i] += s_y[g][cl][ng * TPT + i];
       }
