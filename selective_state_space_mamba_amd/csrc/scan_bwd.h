@@ -152,6 +152,20 @@ __global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ 
   }
 }
 
+// v[r] (r = 0..3) per lane, scaled by f; returns in row r of the wave (lanes
+// 16r..16r+15) the sum over the wave's 4 rows of v[r] at the same column.
+// Swapping lanes 32-63 of one register with lanes 0-31 of another and adding
+// sums the two 32-lane halves (steps 0/1 land in the low half, 2/3 in the
+// high half); the same with odd/even 16-lane rows sums the rows within a half.
+__device__ __forceinline__ float sum_rows4(const float (&v)[4], float f) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0] * f), __float_as_uint(v[2] * f), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[1] * f), __float_as_uint(v[3] * f), false, false);
+  const float z02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float z13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(z02), __float_as_uint(z13), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Lane-mask select: m all ones gives x, all zeros gives y (one v_bfi_b32).
 __device__ __forceinline__ float bsel(uint32_t m, float x, float y) {
   return __uint_as_float((__float_as_uint(x) & m) | (__float_as_uint(y) & ~m));
@@ -191,16 +205,20 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   constexpr int QI = (N * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment
   static_assert(TS % NGP == 0 && TH % 4 == 0, "segment splits over the thread rows");
   static_assert(N <= 16, "one state per thread");
+  constexpr bool KEEP_ABAR = MSCAN_BWD_KEEP_ABAR;
 
   __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ
   __shared__ __attribute__((aligned(16))) float s_u[CB * PS];    // u
   __shared__ __attribute__((aligned(16))) float s_dy[CB * PS];   // dy
   __shared__ __attribute__((aligned(16))) float s_B[N * PS];
   __shared__ __attribute__((aligned(16))) float s_C[N * PS];
-  __shared__ __attribute__((aligned(16))) float s_pd[N][CB][YS];  // per-state parts of dΔ
-  __shared__ __attribute__((aligned(16))) float s_pu[N][CB][YS];  // per-state parts of du
+  // Parts of dΔ and du per wave: each wave first sums its 4 state rows in
+  // registers, so a (position, channel) gathers NW = NGP/4 parts.
+  constexpr int NW = NGP / 4;
+  __shared__ __attribute__((aligned(16))) float s_pd[NW][CB][YS];
+  __shared__ __attribute__((aligned(16))) float s_pu[NW][CB][YS];
   // (the final per-channel sums reuse s_pd: 2·NGP·CB floats, after the last barrier)
-  static_assert(2 * NGP <= N * YS, "room for the final sums");
+  static_assert(2 * NGP <= NW * YS, "room for the final sums");
 
   const int tid = threadIdx.x;
   const int cl = tid % CB;
@@ -208,6 +226,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   const bool nvalid = ng < N;
   const int n = nvalid ? ng : 0;
   const uint32_t m1 = (cl & 2) ? ~0u : 0u, m0 = (cl & 1) ? ~0u : 0u;
+  const float nvf = nvalid ? 1.f : 0.f;  // rows past N (N < 4) add nothing to the state sums
 
   const int nblocks = gridDim.x;
   int bid = logical_block(blockIdx.x, nblocks, 4);
@@ -305,7 +324,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
     if (seg > 0) load_seg(seg - 1, raw);
 
     // ---- recompute the segment's states from its checkpoint ----
-    float hs[TS], as[MSCAN_BWD_KEEP_ABAR ? TS : 1];
+    float hs[TS], as[KEEP_ABAR ? TS : 1];
     {
       float h = h0;
 #pragma unroll
@@ -317,7 +336,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
         const float c = EXACT ? zoh_coef(a, dt * Anat, dt, invA) : dt;
         h = __builtin_fmaf(a, h, c * uu * Bv);
         hs[s] = h;
-        if constexpr (MSCAN_BWD_KEEP_ABAR) as[s] = a;
+        if constexpr (KEEP_ABAR) as[s] = a;
       }
     }
     // The adjoint reads the staged values again from LDS: kept live from the
@@ -343,7 +362,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
             const float dyv = s_dy[cl * PS + s];
             const float Bv = s_B[n * PS + s];
             const float Cv = s_C[n * PS + s];
-            const float a = MSCAN_BWD_KEEP_ABAR ? as[s] : ex2(dt * Al2);
+            const float a = KEEP_ABAR ? as[s] : ex2(dt * Al2);
             const float hp = s > 0 ? hs[s - 1] : h0;
             const float l = __builtin_fmaf(Cv, dyv, carry);  // λ
             const float ga = l * hp;
@@ -365,11 +384,11 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
             pBC[8 + sq] = dyv * hs[s];
             carry = a * l;
           }
-          if (nvalid) {
-            const int sh = qt * 8 + s4;  // position within the half
-            *reinterpret_cast<float4*>(&s_pd[n][cl][sh]) = make_float4(pd4[0], pd4[1], pd4[2], pd4[3]);
-            *reinterpret_cast<float4*>(&s_pu[n][cl][sh]) = make_float4(pu4[0], pu4[1], pu4[2], pu4[3]);
-          }
+          // the 4 steps' parts summed over the wave's 4 state rows: row r of
+          // the wave ends with step r
+          const int sh = qt * 8 + s4 + (ng & 3);  // position within the half
+          s_pd[ng >> 2][cl][sh] = sum_rows4(pd4, nvf);
+          s_pu[ng >> 2][cl][sh] = sum_rows4(pu4, nvf);
         }
         // sums over the row's 16 channels: lane cl < 8 ends with dB of step
         // cl, lane cl >= 8 with dC of step cl - 8
@@ -390,7 +409,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
           const int pp = p0 + s;
           float dd = 0.f, duu = 0.f;
 #pragma unroll
-          for (int g = 0; g < N; ++g) {
+          for (int g = 0; g < NW; ++g) {
             dd += s_pd[g][cl][sh];
             duu += s_pu[g][cl][sh];
           }
