@@ -108,14 +108,14 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 
 // Workspace of the backward pass, in this order (each region 256-byte aligned):
 // the forward recompute's time-split carries, the per-direction fp32 output
-// rows, state checkpoints every 32 positions, dy, the per-channel-block
-// partial sums of dB and dC, the per-direction du of the cross scan, and the
+// rows, state checkpoints every 32 positions, the per-channel-block partial
+// sums of dB and dC, the per-direction du of the cross scan, and the
 // per-batch partial sums of dA, dD and ddelta_bias.
 constexpr int kBwdBlock = 16;  // channels per workgroup of scan_bwd_kernel
 struct BwdPlan {
   Plan fwd;
   int nblk, ntiles;
-  size_t agg, ws_y, ckpt, dy, dB, dC, du, dA, dD, dbias, total;
+  size_t agg, ws_y, ckpt, dB, dC, du, dA, dD, dbias, total;
 };
 
 int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
@@ -141,7 +141,6 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   bp->agg = take(pl.agg_state_bytes + pl.agg_dsum_bytes);
   bp->ws_y = take((size_t)K * Bz * L * Dm * f4);
   bp->ckpt = take((size_t)K * Bz * bp->ntiles * Dm * N * f4);
-  bp->dy = take((size_t)Bz * L * Dm * f4);
   bp->dB = take((size_t)bp->nblk * Bz * K * L * N * f4);
   bp->dC = take((size_t)bp->nblk * Bz * K * L * N * f4);
   bp->du = pl.Ku != K ? take((size_t)K * Bz * L * Dm * f4) : off;
@@ -153,11 +152,11 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
 }
 
 template <typename TIn>
-int launch_bwd_prep(const float* ws_y, const void* z, const void* dout, float* dy, void* dz, int K, int64_t n,
-                    hipStream_t stream) {
+int launch_bwd_dz(const float* ws_y, const void* z, const void* dout, void* dz, int K, int64_t n,
+                  hipStream_t stream) {
   const unsigned blocks = (unsigned)((n / 8 + 255) / 256);
-  hipLaunchKernelGGL((bwd_prep_kernel<TIn>), dim3(blocks), dim3(256), 0, stream, ws_y, static_cast<const TIn*>(z),
-                     static_cast<const TIn*>(dout), dy, static_cast<TIn*>(dz), K, n);
+  hipLaunchKernelGGL((bwd_dz_kernel<TIn>), dim3(blocks), dim3(256), 0, stream, ws_y, static_cast<const TIn*>(z),
+                     static_cast<const TIn*>(dout), static_cast<TIn*>(dz), K, n);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
@@ -322,14 +321,17 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
             : (exact ? dispatch_scan_f32_exact(N, p, pl, stream) : dispatch_scan_f32_simple(N, p, pl, stream));
   if (rc != MAMBA_OK) return rc;
 
-  // 2. dy = dout·silu(z) and dz
+  // 2. dz of several directions (it needs their sum; with one direction the
+  // reverse sweep writes dz while staging)
   const int64_t nrow = dims->batch * dims->seqlen * dims->dim;
-  void* dz_out = z ? dz : nullptr;
-  rc = bf16 ? launch_bwd_prep<uint16_t>(p.ws_y, z, dout, wsf(bp.dy), dz_out, pl.K, nrow, stream)
-            : launch_bwd_prep<float>(p.ws_y, z, dout, wsf(bp.dy), dz_out, pl.K, nrow, stream);
-  if (rc != MAMBA_OK) return rc;
+  const bool dz_here = z && dz && pl.K == 1;
+  if (z && dz && !dz_here) {
+    rc = bf16 ? launch_bwd_dz<uint16_t>(p.ws_y, z, dout, dz, pl.K, nrow, stream)
+              : launch_bwd_dz<float>(p.ws_y, z, dout, dz, pl.K, nrow, stream);
+    if (rc != MAMBA_OK) return rc;
+  }
 
-  // 3. the reverse sweep
+  // 3. the reverse sweep (dy = dout·silu(z) computed while staging)
   BwdParams q{};
   q.u = u;
   q.delta = delta;
@@ -339,7 +341,11 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   q.D = D;
   q.delta_bias = delta_bias;
   q.ckpt = p.ckpt;
-  q.dy = wsf(bp.dy);
+  q.dout = dout;
+  q.z = z;
+  q.ws_y = p.ws_y;
+  q.dz = dz_here ? dz : nullptr;
+  q.dz_here = dz_here ? 1 : 0;
   const bool shared_u = pl.Ku != pl.K;
   q.du = shared_u ? nullptr : du;
   q.du_part = shared_u ? wsf(bp.du) : nullptr;

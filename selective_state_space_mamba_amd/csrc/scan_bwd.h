@@ -8,7 +8,7 @@
 // The training pass recomputes the states instead of storing them [MFS §5;
 // S4M §2.3].  For a loss with gradient dout on the output, per direction k,
 // batch b, channel d and state n (scan position p visiting token t):
-//   dy = dout·silu(z);  dz = dout·y_all·silu'(z)              (bwd_prep_kernel)
+//   dy = dout·silu(z);  dz = dout·y_all·silu'(z)     (staging; bwd_dz_kernel for K > 1)
 //   λ_p = C_t·dy_t + Ā_{p+1}·λ_{p+1}                           (adjoint of h_p)
 //   dΔ_p = Σ_n [λ h_{p-1} A Ā + λ (∂B̄/∂Δ)·u],  du_t = Σ_n λ B̄_n + D·dy_t
 //   dA += λ h_{p-1} Δ Ā (+ λ (∂c/∂A) B u for the exact rule)
@@ -74,7 +74,11 @@ struct BwdParams {
   const float* D;           // may be null
   const float* delta_bias;  // may be null
   const float* ckpt;        // [K][Bsz][ntiles][Dm][N] states at every 32-position tile start
-  const float* dy;          // [Bsz][L][Dm] float32
+  const void* dout;         // [Bsz][L][Dm]
+  const void* z;            // [Bsz][L][Dm] or null (no gate)
+  const float* ws_y;        // [K][Bsz][L][Dm] ungated output rows of the forward recompute
+  void* dz;                 // [Bsz][L][Dm]: written while staging when dz_here
+  int dz_here;              // one direction and a gate: dz from this direction's row
   void* du;                 // [Bsz][Ku][L][Dm] (Ku = K), or null when du_part is used
   float* du_part;           // [K][Bsz][L][Dm] (the cross scan shares u), or null
   void* ddelta;             // [Bsz][K][L][Dm]
@@ -87,45 +91,34 @@ struct BwdParams {
   int Bsz, Dm, L, H, W, K, Ku, kinds, nblk_d, ntiles, softplus;
 };
 
-// dy = dout·silu(z), dz = dout·y_all·silu'(z) with y_all = Σ_k y_k (ungated);
-// without a gate dy = dout.  Eight consecutive elements per thread (n is a
-// multiple of 8: the channel count is).
+// dz = dout·y_all·silu'(z), y_all = Σ_k y_k (ungated), silu'(z) = σ(z)·(1 + z·(1 - σ(z))),
+// for several directions (with one, scan_bwd_kernel writes dz while staging).
+// Eight consecutive elements per thread (n is a multiple of 8: the channel
+// count is).
 template <typename TIn>
-__global__ void __launch_bounds__(256) bwd_prep_kernel(const float* __restrict__ ws_y, const TIn* __restrict__ z,
-                                                       const TIn* __restrict__ dout, float* __restrict__ dy,
-                                                       TIn* __restrict__ dz, int K, int64_t n) {
+__global__ void __launch_bounds__(256) bwd_dz_kernel(const float* __restrict__ ws_y, const TIn* __restrict__ z,
+                                                     const TIn* __restrict__ dout, TIn* __restrict__ dz, int K,
+                                                     int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= n) return;
-  Vec<TIn, 8> go;
+  Vec<TIn, 8> go, zv;
   go.load(dout + i);
-  float d8[8];
-  if (z == nullptr) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) d8[c] = go.get(c);
-    storeV<8>(dy + i, d8);
-    return;
-  }
-  Vec<TIn, 8> zv;
   zv.load(z + i);
   float y8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (dz) {
-    for (int k = 0; k < K; ++k) {
-      Vec<float, 8> yk;
-      yk.load(ws_y + k * n + i);
+  for (int k = 0; k < K; ++k) {
+    Vec<float, 8> yk;
+    yk.load(ws_y + k * n + i);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) y8[c] += yk.get(c);
-    }
+    for (int c = 0; c < 8; ++c) y8[c] += yk.get(c);
   }
   float g8[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float zz = zv.get(c), g = go.get(c);
+    const float zz = zv.get(c);
     const float sg = rcp(1.0f + ex2(-zz * kLog2e));
-    d8[c] = g * zz * sg;
-    g8[c] = g * y8[c] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+    g8[c] = go.get(c) * y8[c] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
   }
-  storeV<8>(dy + i, d8);
-  if (dz) storeV<8>(dz + i, g8);
+  storeV<8>(dz + i, g8);
 }
 
 // out[i] = Σ_s in[s·stride + i], s = 0 .. nslices-1 in order; V consecutive
@@ -252,7 +245,13 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   const TIn* dl_s = static_cast<const TIn*>(p.delta) + (int64_t)(b * p.K + k) * L * D;
   const TIn* B_s = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* C_s = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
-  const float* dy_s = p.dy + (int64_t)b * L * D;
+  const TIn* go_s = static_cast<const TIn*>(p.dout) + (int64_t)b * L * D;
+  const bool gated = p.z != nullptr;
+  const TIn* z_s = gated ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : go_s;  // (no gate: unused loads)
+  // the direction's fp32 output row for dz; without dz_here every lane loads
+  // element 0 (one cache line, unused)
+  const float* y_s = p.ws_y + ((int64_t)k * p.Bsz + b) * L * D;
+  const int64_t y_mask = p.dz_here ? ~(int64_t)0 : 0;
   const float* ck_s = p.ckpt + ((int64_t)k * p.Bsz + b) * p.ntiles * D * N;
   const bool own = nvalid && dvalid;  // this thread's (channel, state) exists
   const int64_t ck_off = own ? (int64_t)d * N + n : 0;
@@ -266,8 +265,8 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   // raw global values of one segment (rows clamped into the sequence; padded
   // rows are zeroed at staging)
   struct Raw {
-    TIn dl[TPS], u[TPS], B[QI], C[QI];
-    float dy[TPS], h0;
+    TIn dl[TPS], u[TPS], go[TPS], zr[TPS], B[QI], C[QI];
+    float y[TPS], h0;
   };
   auto load_seg = [&](int seg, Raw& r) __attribute__((always_inline)) {
     const int p0 = seg * TS;
@@ -276,7 +275,9 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
       const int64_t off = (int64_t)token(min(p0 + ng * TPS + i, L - 1)) * D + dc;
       r.dl[i] = dl_s[off];
       r.u[i] = u_s[off];
-      r.dy[i] = dy_s[off];
+      r.go[i] = go_s[off];
+      r.zr[i] = z_s[off];
+      r.y[i] = y_s[off & y_mask];
     }
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
@@ -296,7 +297,18 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
       const float x = to_f32(r.dl[i]) + bias;
       s_dt[cl * PS + tt] = (p.softplus ? softplus_log2(x) * kLn2 : x) * okf;
       s_u[cl * PS + tt] = to_f32(r.u[i]) * okf;
-      s_dy[cl * PS + tt] = r.dy[i] * okf;
+      // dy = dout·silu(z); with one direction also dz = dout·y·silu'(z)
+      const float g = to_f32(r.go[i]);
+      float dyv = g;
+      if (gated) {
+        const float zz = to_f32(r.zr[i]);
+        const float sg = rcp(1.0f + ex2(-zz * kLog2e));
+        dyv = g * zz * sg;
+        if (p.dz_here && p0 + tt < L && dvalid)
+          store1(static_cast<TIn*>(p.dz) + ((int64_t)b * L + token(p0 + tt)) * D + d,
+                 g * r.y[i] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
+      }
+      s_dy[cl * PS + tt] = dyv * okf;
     }
 #pragma unroll
     for (int i = 0; i < QI; ++i) {

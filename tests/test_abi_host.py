@@ -138,9 +138,9 @@ def test_conv1d_validation(lib):
 def test_bwd_workspace_and_validation(lib):
     d = dims()
     need = ms.bwd_workspace_bytes(d, ms.DIR_FWD)
-    # at least: per-direction fp32 rows, dy, 32-step checkpoints, dB/dC partials per 16-channel block
+    # at least: per-direction fp32 rows, 32-step checkpoints, dB/dC partials per 16-channel block
     L, Dm, N, Bz = 100, 64, 16, 2
-    assert need >= 4 * (Bz * L * Dm * 2 + Bz * 4 * Dm * N + 2 * (Dm // 16) * Bz * L * N)
+    assert need >= 4 * (Bz * L * Dm + Bz * 4 * Dm * N + 2 * (Dm // 16) * Bz * L * N)
     assert need % 256 == 0 and ms.bwd_workspace_bytes(d, ms.DIR_FWD) == need
     cross = ms.bwd_workspace_bytes(dims(seqlen=96, height=8, width=12), ms.DIR_CROSS2D)
     assert cross >= 4 * 4 * Bz * 96 * Dm * 2  # per-direction rows and per-direction du
