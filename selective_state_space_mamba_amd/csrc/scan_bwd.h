@@ -129,8 +129,23 @@ __global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ 
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= n) return;
   if constexpr (V == 4) {
+    // 16 slices' loads in flight per thread (the sum stays in slice order)
+    constexpr int U = 16;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t s = 0; s < nslices; ++s) {
+    int64_t s = 0;
+    for (; s + U <= nslices; s += U) {
+      float4 v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) v[j] = *reinterpret_cast<const float4*>(in + (s + j) * stride + i);
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        acc[0] += v[j].x;
+        acc[1] += v[j].y;
+        acc[2] += v[j].z;
+        acc[3] += v[j].w;
+      }
+    }
+    for (; s < nslices; ++s) {
       const float4 v = *reinterpret_cast<const float4*>(in + s * stride + i);
       acc[0] += v.x;
       acc[1] += v.y;
