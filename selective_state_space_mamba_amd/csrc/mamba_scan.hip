@@ -160,17 +160,22 @@ int launch_bwd_dz(const float* ws_y, const void* z, const void* dout, void* dz, 
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 
-// (stride == n at every call: the partial slices are packed)
+// Sums over packed partial slices (stride == n at every call); a second
+// (in1, out1) pair of the same shape, if given, shares the launch.
 template <typename TOut>
-int launch_bwd_sum(const float* in, int64_t nslices, int64_t stride, int64_t n, void* out, hipStream_t stream) {
+int launch_bwd_sum(const float* in, int64_t nslices, int64_t stride, int64_t n, void* out, hipStream_t stream,
+                   const float* in1 = nullptr, void* out1 = nullptr) {
+  const unsigned pairs = in1 ? 2u : 1u;
+  TOut* o0 = static_cast<TOut*>(out);
+  TOut* o1 = static_cast<TOut*>(in1 ? out1 : out);
   if (n % 4 == 0 && stride % 4 == 0) {
     const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
-    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 4>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
-                       static_cast<TOut*>(out));
+    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 4>), dim3(blocks, pairs), dim3(256), 0, stream, in, o0,
+                       in1 ? in1 : in, o1, nslices, stride, n);
   } else {
     const unsigned blocks = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 1>), dim3(blocks), dim3(256), 0, stream, in, nslices, stride, n,
-                       static_cast<TOut*>(out));
+    hipLaunchKernelGGL((bwd_sum_kernel<TOut, 1>), dim3(blocks, pairs), dim3(256), 0, stream, in, o0,
+                       in1 ? in1 : in, o1, nslices, stride, n);
   }
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
@@ -376,17 +381,18 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   const int64_t K = pl.K, Bz = dims->batch, Dm = dims->dim;
   const int64_t nbc = Bz * K * dims->seqlen * N;
   if (bf16) {
-    rc = launch_bwd_sum<uint16_t>(q.dB_part, bp.nblk, nbc, nbc, dB, stream);
-    if (rc == MAMBA_OK) rc = launch_bwd_sum<uint16_t>(q.dC_part, bp.nblk, nbc, nbc, dC, stream);
+    rc = launch_bwd_sum<uint16_t>(q.dB_part, bp.nblk, nbc, nbc, dB, stream, q.dC_part, dC);
     if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<uint16_t>(q.du_part, K, nrow, nrow, du, stream);
   } else {
-    rc = launch_bwd_sum<float>(q.dB_part, bp.nblk, nbc, nbc, dB, stream);
-    if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dC_part, bp.nblk, nbc, nbc, dC, stream);
+    rc = launch_bwd_sum<float>(q.dB_part, bp.nblk, nbc, nbc, dB, stream, q.dC_part, dC);
     if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<float>(q.du_part, K, nrow, nrow, du, stream);
   }
   if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dA_part, Bz, K * Dm * N, K * Dm * N, dA, stream);
-  if (rc == MAMBA_OK && dD) rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream);
-  if (rc == MAMBA_OK && ddelta_bias)
+  if (rc == MAMBA_OK && dD && ddelta_bias)
+    rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream, q.dbias_part, ddelta_bias);
+  else if (rc == MAMBA_OK && dD)
+    rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream);
+  else if (rc == MAMBA_OK && ddelta_bias)
     rc = launch_bwd_sum<float>(q.dbias_part, Bz, K * Dm, K * Dm, ddelta_bias, stream);
   return rc;
 }

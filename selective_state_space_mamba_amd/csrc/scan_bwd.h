@@ -122,10 +122,15 @@ __global__ void __launch_bounds__(256) bwd_dz_kernel(const float* __restrict__ w
 }
 
 // out[i] = Σ_s in[s·stride + i], s = 0 .. nslices-1 in order; V consecutive
-// elements per thread (V = 4 needs n and stride multiples of 4).
+// elements per thread (V = 4 needs n and stride multiples of 4).  blockIdx.y
+// selects one of two independent (in, out) pairs, so that two sums share a
+// launch.
 template <typename TOut, int V>
-__global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ in, int64_t nslices, int64_t stride,
-                                                      int64_t n, TOut* __restrict__ out) {
+__global__ void __launch_bounds__(256) bwd_sum_kernel(const float* __restrict__ in0, TOut* __restrict__ out0,
+                                                      const float* __restrict__ in1, TOut* __restrict__ out1,
+                                                      int64_t nslices, int64_t stride, int64_t n) {
+  const float* __restrict__ in = blockIdx.y == 0 ? in0 : in1;
+  TOut* __restrict__ out = blockIdx.y == 0 ? out0 : out1;
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= n) return;
   if constexpr (V == 4) {
