@@ -93,6 +93,13 @@ SMALL = [
      False),
     ("split_fwd_bf16", W("split_fwd_bf16", 1, 64, 4133, 16, I.DIR_FWD, "bf16", True, 39), True, False, True, True),
     ("split_bidir_f32", W("split_bidir_f32", 1, 16, 2500, 8, I.DIR_BIDIR, "f32", True, 42), True, True, False, True),
+    # edge cases: one position, half a channel block, segment boundaries, a one-row grid
+    ("L1_D8_bf16_n2", W("L1_D8", 1, 8, 1, 2, I.DIR_FWD, "bf16", True, 44), True, False, True, True),
+    ("L31_bidir_f32", W("L31_bidir", 2, 24, 31, 16, I.DIR_BIDIR, "f32", True, 45), True, False, False, True),
+    ("L33_bwd_bf16_n4", W("L33_bwd", 3, 40, 33, 4, I.DIR_BWD, "bf16", False, 46), True, False, True, True),
+    ("L32_fwd_f32_n1", W("L32_fwd", 1, 16, 32, 1, I.DIR_FWD, "f32", True, 47), True, False, False, False),
+    ("grid_1x37_f32", W("grid_1x37", 1, 16, 37, 8, I.DIR_CROSS2D, "f32", True, 48, 1, 37), True, False, True, True),
+    ("exact_nosoftplus_init_bf16", W("ex_nsp", 2, 32, 65, 16, I.DIR_FWD, "bf16", True, 49), False, True, True, True),
 ]
 
 
@@ -106,7 +113,10 @@ def test_bwd_small(case):
         x["delta_bias"] = None
     if not softplus:  # Δ = delta itself: keep it positive
         r = np.random.Generator(np.random.PCG64([w.seed, 4]))
-        x["delta"] = r.uniform(0.01, 0.3, x["delta"].shape).astype(np.float32)
+        dl = r.uniform(0.01, 0.3, x["delta"].shape).astype(np.float32)
+        x["delta"] = I.bf16_bits(dl) if w.dtype == "bf16" else dl
+        if x["delta_bias"] is not None:  # the inverse-softplus bias would make Δ negative
+            x["delta_bias"] = r.uniform(0.0, 0.05, x["delta_bias"].shape).astype(np.float32)
     dout = I.make_dout(w)
     init = init_state(w, w.seed) if with_init else None
     got = gpu_bwd(w, x, dout, softplus=softplus, exact=exact, init=init)
