@@ -51,7 +51,8 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   const int64_t es = g->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;
   // (64 rows of margin: prefetches past either end of the sequence must still
   // map to offsets outside the slice without wrapping)
-  if ((g->seqlen + 64) * g->dim * es > INT32_MAX || (K > 1 && g->seqlen * g->dim * 4 > INT32_MAX))
+  // (fp32 rows: at most 2^31 bytes per slice, so every offset stays below 2^31)
+  if ((g->seqlen + 64) * g->dim * es > INT32_MAX || (K > 1 && g->seqlen * g->dim * 4 > ((int64_t)1 << 31)))
     return MAMBA_ERR_UNSUPPORTED;
   pl->K = K;
   pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
@@ -109,13 +110,16 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 // Workspace of the backward pass, in this order (each region 256-byte aligned):
 // the forward recompute's time-split carries, the per-direction fp32 output
 // rows, state checkpoints every 32 positions, the per-channel-block partial
-// sums of dB and dC, the per-direction du of the cross scan, and the
-// per-batch partial sums of dA, dD and ddelta_bias.
-constexpr int kBwdBlock = 16;  // channels per workgroup of scan_bwd_kernel
+// sums of dB and dC, the per-direction du of the cross scan, the per-chunk
+// and per-batch partial sums of dA, dD and ddelta_bias, and the adjoint's
+// time-split carries.
+constexpr int kBwdBlock = 16;     // channels per workgroup of scan_bwd_kernel
+constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per CU)
+constexpr int kBwdMinChunk = 1024;  // shortest time chunk of a split adjoint
 struct BwdPlan {
   Plan fwd;
-  int nblk, ntiles;
-  size_t agg, ws_y, ckpt, dB, dC, du, dA, dD, dbias, total;
+  int nblk, ntiles, nchunks, chunk_len;
+  size_t agg, ws_y, ckpt, dB, dC, du, dA, dD, dbias, bagg_S, bagg_dsum, total;
 };
 
 int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
@@ -124,12 +128,27 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   // one state per thread and 32-position checkpoints (the forward tile)
   if (g->dstate > 16 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
   // the recompute always keeps per-direction fp32 rows (32-bit slice offsets)
-  if (g->seqlen * g->dim * 4 > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  if (g->seqlen * g->dim * 4 > ((int64_t)1 << 31)) return MAMBA_ERR_UNSUPPORTED;
   const Plan& pl = bp->fwd;
   const int64_t K = pl.K, Bz = g->batch, L = g->seqlen, Dm = g->dim, N = g->dstate;
   bp->nblk = (int)((Dm + kBwdBlock - 1) / kBwdBlock);
   bp->ntiles = (int)((L + kTile - 1) / kTile);
-  if ((int64_t)bp->nblk * Bz * K > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  // Time split of the adjoint when its rows fill less than one round of
+  // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
+  const int64_t rows = (int64_t)bp->nblk * Bz * K;
+  int64_t nch = 1;
+  if (rows < kBwdSlots) {
+    nch = (2 * kBwdSlots + rows - 1) / rows;
+    if (nch > L / kBwdMinChunk) nch = L / kBwdMinChunk;
+    if (nch > 256) nch = 256;
+    if (nch < 1) nch = 1;
+  }
+  int64_t clen = (L + nch - 1) / nch;
+  clen = (clen + kTile - 1) / kTile * kTile;
+  nch = (L + clen - 1) / clen;
+  bp->nchunks = (int)nch;
+  bp->chunk_len = (int)clen;
+  if (rows * nch > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t f4 = sizeof(float);
   size_t off = 0;
@@ -144,9 +163,11 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   bp->dB = take((size_t)bp->nblk * Bz * K * L * N * f4);
   bp->dC = take((size_t)bp->nblk * Bz * K * L * N * f4);
   bp->du = pl.Ku != K ? take((size_t)K * Bz * L * Dm * f4) : off;
-  bp->dA = take((size_t)Bz * K * Dm * N * f4);
-  bp->dD = take((size_t)Bz * K * Dm * f4);
-  bp->dbias = take((size_t)Bz * K * Dm * f4);
+  bp->dA = take((size_t)nch * Bz * K * Dm * N * f4);
+  bp->dD = take((size_t)nch * Bz * K * Dm * f4);
+  bp->dbias = take((size_t)nch * Bz * K * Dm * f4);
+  bp->bagg_S = take((size_t)K * Bz * (nch - 1) * Dm * N * f4);
+  bp->bagg_dsum = take((size_t)K * Bz * (nch - 1) * Dm * f4);
   bp->total = off;
   return MAMBA_OK;
 }
@@ -371,6 +392,10 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   q.kinds = p.kinds;
   q.nblk_d = bp.nblk;
   q.ntiles = bp.ntiles;
+  q.nchunks = bp.nchunks;
+  q.chunk_len = bp.chunk_len;
+  q.agg_S = wsf(bp.bagg_S);
+  q.agg_dsum = wsf(bp.bagg_dsum);
   q.softplus = p.softplus;
   rc = bf16 ? (exact ? dispatch_bwd_bf16_exact(N, q, stream) : dispatch_bwd_bf16_simple(N, q, stream))
             : (exact ? dispatch_bwd_f32_exact(N, q, stream) : dispatch_bwd_f32_simple(N, q, stream));
@@ -387,13 +412,15 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
     rc = launch_bwd_sum<float>(q.dB_part, bp.nblk, nbc, nbc, dB, stream, q.dC_part, dC);
     if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<float>(q.du_part, K, nrow, nrow, du, stream);
   }
-  if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dA_part, Bz, K * Dm * N, K * Dm * N, dA, stream);
+  // (the dA, dD, ddelta_bias parts are [chunk][batch][K][...]: one slice per (chunk, batch))
+  const int64_t nsl = (int64_t)bp.nchunks * Bz;
+  if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dA_part, nsl, K * Dm * N, K * Dm * N, dA, stream);
   if (rc == MAMBA_OK && dD && ddelta_bias)
-    rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream, q.dbias_part, ddelta_bias);
+    rc = launch_bwd_sum<float>(q.dD_part, nsl, K * Dm, K * Dm, dD, stream, q.dbias_part, ddelta_bias);
   else if (rc == MAMBA_OK && dD)
-    rc = launch_bwd_sum<float>(q.dD_part, Bz, K * Dm, K * Dm, dD, stream);
+    rc = launch_bwd_sum<float>(q.dD_part, nsl, K * Dm, K * Dm, dD, stream);
   else if (rc == MAMBA_OK && ddelta_bias)
-    rc = launch_bwd_sum<float>(q.dbias_part, Bz, K * Dm, K * Dm, ddelta_bias, stream);
+    rc = launch_bwd_sum<float>(q.dbias_part, nsl, K * Dm, K * Dm, ddelta_bias, stream);
   return rc;
 }
 

@@ -84,10 +84,15 @@ struct BwdParams {
   void* ddelta;             // [Bsz][K][L][Dm]
   float* dB_part;           // [nblk_d][Bsz][K][L][N]
   float* dC_part;           // [nblk_d][Bsz][K][L][N]
-  float* dA_part;           // [Bsz][K][Dm][N]
-  float* dD_part;           // [Bsz][K][Dm]
-  float* dbias_part;        // [Bsz][K][Dm]
+  float* dA_part;           // [nchunks][Bsz][K][Dm][N]
+  float* dD_part;           // [nchunks][Bsz][K][Dm]
+  float* dbias_part;        // [nchunks][Bsz][K][Dm]
   float* dinit;             // [Bsz][K][Dm][N] or null
+  // time split: the adjoint of chunk c starts from the carry of chunks c+1..
+  float* agg_S;             // [K][Bsz][nchunks-1][Dm][N]: carry out of chunk j >= 1 from a zero carry in
+  float* agg_dsum;          // [K][Bsz][nchunks-1][Dm]: ΣΔ over chunk j
+  int nchunks, chunk_len;   // chunks per sequence (chunk_len a multiple of 32)
+  int chunk0, grid_chunks;  // chunks chunk0 .. chunk0+grid_chunks-1 are this launch's
   int Bsz, Dm, L, H, W, K, Ku, kinds, nblk_d, ntiles, softplus;
 };
 
@@ -198,13 +203,20 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
   return bsel(m0, r2[1], r2[0]) + bwd_quad_perm_xor1(bsel(m0, r2[0], r2[1]));  // step j
 }
 
-// One workgroup: 16 channels of one (direction, batch) for the whole
-// sequence, walked backwards.  Thread tid: channel cl = tid % 16, state
+// One workgroup: 16 channels of one (direction, batch) over one time chunk
+// (the whole sequence unless it is split), walked backwards.  Thread tid: channel cl = tid % 16, state
 // n = tid / 16 (rows n >= N only pad small N to a whole wave).  The global
 // loads of the next (earlier) segment are issued before the current one is
 // computed, and the staged rows hold Δ in natural units (the exp takes
 // A·log2 e).
-template <typename TIn, int N, bool EXACT>
+//
+// AGG: the aggregate pass of a time split.  It runs only the adjoint carry
+// (λ = C·dy + carry, carry = Ā·λ, which needs no states) from a zero carry at
+// the chunk's end and stores the carry out of the chunk and its ΣΔ; the main
+// pass then starts chunk c from the fold over the later chunks j,
+// carry <- S_j + e^{A·ΣΔ_j}·carry (the carry's dependence on its start value
+// is the product of the chunk's decays).
+template <typename TIn, int N, bool EXACT, bool AGG>
 __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
   constexpr int NGP = N < 4 ? 4 : N;  // thread rows
@@ -245,10 +257,14 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   int bid = logical_block(blockIdx.x, nblocks, 4);
   const int dblk = bid % p.nblk_d;
   bid /= p.nblk_d;
+  const int c = p.chunk0 + bid % p.grid_chunks;
+  bid /= p.grid_chunks;
   const int b = bid % p.Bsz;
   const int k = bid / p.Bsz;
 
   const int D = p.Dm, L = p.L;
+  const int seg_lo = c * p.chunk_len / TS;                            // the chunk's first segment
+  const int seg_hi = (min(L, (c + 1) * p.chunk_len) + TS - 1) / TS - 1;  // and its last
   const int d0 = dblk * CB;
   const int d = d0 + cl;
   const bool dvalid = d < D;
@@ -294,19 +310,21 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
     for (int i = 0; i < TPS; ++i) {
       const int64_t off = (int64_t)token(min(p0 + ng * TPS + i, L - 1)) * D + dc;
       r.dl[i] = dl_s[off];
-      r.u[i] = u_s[off];
       r.go[i] = go_s[off];
       r.zr[i] = z_s[off];
-      r.y[i] = y_s[off & y_mask];
+      if constexpr (!AGG) {
+        r.u[i] = u_s[off];
+        r.y[i] = y_s[off & y_mask];
+      }
     }
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
       const int q = min(tid + i * NT, N * TS - 1);
       const int64_t off = (int64_t)token(min(p0 + q / N, L - 1)) * N + q % N;
-      r.B[i] = B_s[off];
+      if constexpr (!AGG) r.B[i] = B_s[off];
       r.C[i] = C_s[off];
     }
-    r.h0 = ck_s[(int64_t)seg * D * N + ck_off];
+    if constexpr (!AGG) r.h0 = ck_s[(int64_t)seg * D * N + ck_off];
   };
   auto stage_seg = [&](int seg, const Raw& r) __attribute__((always_inline)) {
     const int p0 = seg * TS;
@@ -316,7 +334,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
       const float okf = (p0 + tt < L && dvalid) ? 1.f : 0.f;
       const float x = to_f32(r.dl[i]) + bias;
       s_dt[cl * PS + tt] = (p.softplus ? softplus_log2(x) * kLn2 : x) * okf;
-      s_u[cl * PS + tt] = to_f32(r.u[i]) * okf;
+      if constexpr (!AGG) s_u[cl * PS + tt] = to_f32(r.u[i]) * okf;
       // dy = dout·silu(z); with one direction also dz = dout·y·silu'(z)
       const float g = to_f32(r.go[i]);
       float dyv = g;
@@ -324,7 +342,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
         const float zz = to_f32(r.zr[i]);
         const float sg = rcp(1.0f + ex2(-zz * kLog2e));
         dyv = g * zz * sg;
-        if (p.dz_here && p0 + tt < L && dvalid)
+        if (!AGG && p.dz_here && p0 + tt < L && dvalid)
           store1(static_cast<TIn*>(p.dz) + ((int64_t)b * L + token(p0 + tt)) * D + d,
                  g * r.y[i] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
       }
@@ -335,25 +353,46 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
       const int q = tid + i * NT;
       if (QI * NT == N * TS || q < N * TS) {
         const float okf = p0 + q / N < L ? 1.f : 0.f;
-        s_B[(q % N) * PS + q / N] = to_f32(r.B[i]) * okf;
+        if constexpr (!AGG) s_B[(q % N) * PS + q / N] = to_f32(r.B[i]) * okf;
         s_C[(q % N) * PS + q / N] = to_f32(r.C[i]) * okf;
       }
     }
   };
 
   float carry = 0.f;  // Ā_{p+1}·λ_{p+1}
-  float dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f;
+  if constexpr (!AGG) {
+    // the carry into this chunk: fold the later chunks' aggregates
+    if (own) {
+      const int64_t arow = ((int64_t)k * p.Bsz + b) * (p.nchunks - 1);
+      for (int j = p.nchunks - 1; j > c; --j) {
+        const int64_t r = arow + (j - 1);
+        carry = __builtin_fmaf(ex2(p.agg_dsum[r * D + d] * Al2), carry, p.agg_S[(r * D + d) * N + n]);
+      }
+    }
+  }
+  float dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f, dsum = 0.f;
 
   Raw raw;
-  load_seg(p.ntiles - 1, raw);
+  load_seg(seg_hi, raw);
   // (Every read of the staging arrays comes before the last barrier of the
   // previous segment, so staging needs no barrier of its own.)
-  for (int seg = p.ntiles - 1; seg >= 0; --seg) {
+  for (int seg = seg_hi; seg >= seg_lo; --seg) {
     const int p0 = seg * TS;
     stage_seg(seg, raw);
-    const float h0 = own ? raw.h0 : 0.f;
+    const float h0 = (!AGG && own) ? raw.h0 : 0.f;  // (before the prefetch overwrites raw)
     __syncthreads();
-    if (seg > 0) load_seg(seg - 1, raw);
+    if (seg > seg_lo) load_seg(seg - 1, raw);
+
+    if constexpr (AGG) {
+#pragma unroll 8
+      for (int s = TS - 1; s >= 0; --s) {
+        const float dt = s_dt[cl * PS + s];
+        const float l = __builtin_fmaf(s_C[n * PS + s], s_dy[cl * PS + s], carry);
+        carry = ex2(dt * Al2) * l;
+        dsum += dt;
+      }
+      __syncthreads();  // the staging arrays are rewritten by the next segment
+    } else {
 
     // ---- recompute the segment's states from its checkpoint ----
     float hs[TS], as[KEEP_ABAR ? TS : 1];
@@ -463,6 +502,16 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
       }
       __syncthreads();  // the partial rows are rewritten by the next half
     }
+    }  // !AGG
+  }
+
+  if constexpr (AGG) {
+    if (dvalid) {
+      const int64_t r = ((int64_t)k * p.Bsz + b) * (p.nchunks - 1) + (c - 1);
+      if (nvalid) p.agg_S[(r * D + d) * N + n] = carry;
+      if (ng == 0) p.agg_dsum[r * D + d] = dsum;
+    }
+    return;
   }
 
   // ---- per-(b, k, d) and per-(b, k, d, n) results ----
@@ -473,8 +522,8 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
   if (dvalid) {
     if (nvalid) {
       const int64_t o = (((int64_t)b * p.K + k) * D + d) * N + n;
-      p.dA_part[o] = dA_acc;
-      if (p.dinit) p.dinit[o] = carry;
+      p.dA_part[(int64_t)c * p.Bsz * p.K * D * N + o] = dA_acc;
+      if (p.dinit && c == 0) p.dinit[o] = carry;
     }
     if (ng == 0) {
       float sD = 0.f, sb = 0.f;
@@ -483,8 +532,9 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bw
         sD += s_red[g * CB + cl];
         sb += s_red[(NGP + g) * CB + cl];
       }
-      p.dD_part[((int64_t)b * p.K + k) * D + d] = sD;
-      p.dbias_part[((int64_t)b * p.K + k) * D + d] = sb;
+      const int64_t o = (((int64_t)c * p.Bsz + b) * p.K + k) * D + d;
+      p.dD_part[o] = sD;
+      p.dbias_part[o] = sb;
     }
   }
 }

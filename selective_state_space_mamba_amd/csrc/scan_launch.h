@@ -145,10 +145,19 @@ int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
 }
 
 template <typename TIn, int N, bool EXACT>
-int launch_bwd(const BwdParams& p, hipStream_t stream) {
+int launch_bwd(BwdParams p, hipStream_t stream) {
   constexpr int NT = 16 * (N < 4 ? 4 : N);
-  const unsigned blocks = (unsigned)(p.nblk_d * p.Bsz * p.K);
-  hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
+  if (p.nchunks > 1) {  // aggregate pass over chunks 1.. (the carry alone: no input-term rule)
+    p.chunk0 = 1;
+    p.grid_chunks = p.nchunks - 1;
+    const unsigned blocks = (unsigned)(p.nblk_d * p.grid_chunks * p.Bsz * p.K);
+    hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, false, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  p.chunk0 = 0;
+  p.grid_chunks = p.nchunks;
+  const unsigned blocks = (unsigned)(p.nblk_d * p.grid_chunks * p.Bsz * p.K);
+  hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, EXACT, false>), dim3(blocks), dim3(NT), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
 

@@ -167,13 +167,17 @@ def test_bwd_optional_outputs_absent():
         assert t.equal(part[k], full[k]), k
 
 
-FULL = ["mamba130m_layer", "vim_bidir_224", "vmamba_ss2d"]
+# (workload, check whole batch items): the 97k-token Vim image has one batch
+# item, which the oracle would need over every channel (minutes); its dB and
+# dC are covered by the split cases above at smaller sizes.
+FULL = [("mamba130m_layer", True), ("vim_bidir_224", True), ("vmamba_ss2d", True), ("vim_bidir_1248", False)]
 
 
-@pytest.mark.parametrize("wname", FULL)
-def test_bwd_full_size(wname):
-    """The full workload on the GPU; the oracle on 24 channels over the whole
-    batch and on the first and last batch items over every channel."""
+@pytest.mark.parametrize("wname,items", FULL, ids=[f[0] for f in FULL])
+def test_bwd_full_size(wname, items):
+    """The full workload on the GPU (the long one with a time-split adjoint);
+    the oracle on 24 channels over the whole batch and, where affordable, on
+    the first and last batch items over every channel."""
     w = I.WORKLOADS[wname]
     announce("bwd full %s" % (w,))
     x = I.make_inputs(w)
@@ -196,7 +200,7 @@ def test_bwd_full_size(wname):
     compare(wname + " channels", ws, got, ref, keys=("du", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dinit"),
             index=chan)
     # whole batch items: dB, dC
-    for b in (0, w.batch - 1):
+    for b in ((0, w.batch - 1) if items else ()):
         xb = dict(x)
         for k in ("u", "delta", "z", "B", "C"):
             xb[k] = None if x[k] is None else np.ascontiguousarray(x[k][b:b + 1])
@@ -204,3 +208,31 @@ def test_bwd_full_size(wname):
         refb = oracle_bwd(wb, xb, np.ascontiguousarray(dout[b:b + 1]))
         compare("%s batch %d" % (wname, b), wb, got, refb, keys=("dB", "dC", "du"),
                 index=lambda k, v: v[b:b + 1])
+
+
+def test_bwd_long_context_channels():
+    """The long-context workload (one batch item, 262,144 tokens: fp32 output
+    rows of exactly 2^31 bytes and an 8-chunk time-split adjoint), checked on
+    24 channels; the gradients are sliced on the GPU before the copy back."""
+    w = I.WORKLOADS["long_context"]
+    announce("bwd full %s (channel subset)" % (w,))
+    x = I.make_inputs(w)
+    dout = I.make_dout(w)
+    xd = dev_inputs(x)
+    g = ms.scan_bwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd["D"], xd["z"], xd["delta_bias"],
+                    dout=to_dev(dout))
+    r = np.random.Generator(np.random.PCG64([w.seed, 5]))
+    S = np.unique(np.concatenate([[0, w.dim - 1], r.choice(w.dim, 22, replace=False)]))
+    St = torch().from_numpy(S).to("cuda:0")
+    got = {k: from_dev(v.index_select(-2 if k in ("dA", "dinit") else -1, St))
+           for k, v in g.items() if k in ("du", "ddelta", "dz", "dA", "dD", "ddelta_bias", "dinit")}
+    del g, xd
+    xs = dict(x)
+    for k in ("u", "delta", "z"):
+        xs[k] = np.ascontiguousarray(x[k][..., S])
+    xs["A"] = np.ascontiguousarray(x["A"][..., S, :])
+    xs["D"] = np.ascontiguousarray(x["D"][..., S])
+    xs["delta_bias"] = np.ascontiguousarray(x["delta_bias"][..., S])
+    ws = w.with_(dim=len(S))
+    ref = oracle_bwd(ws, xs, np.ascontiguousarray(dout[..., S]))
+    compare("long_context channels", ws, got, ref, keys=tuple(got))
