@@ -63,27 +63,24 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   const int64_t waves0 = rows64 * (threads_of((int)N, 0) / 64);
   int layout = 0;
   int64_t nch = 1;
-  auto split = [&](int64_t waves) {
-    int64_t c = (MSCAN_TARGET_WAVES + waves - 1) / waves;
+  auto split = [&](int64_t waves, int64_t target) {
+    int64_t c = (target + waves - 1) / waves;
     if (c > L / MSCAN_MIN_CHUNK) c = L / MSCAN_MIN_CHUNK;
     if (c > MSCAN_MAX_CHUNKS) c = MSCAN_MAX_CHUNKS;
     return c < 1 ? (int64_t)1 : c;
   };
-  // Measured on MI355X: layout 0 is fastest whenever it yields at least 1.5
-  // waves per SIMD, and for long sequences split in time; short sequences with
-  // few rows are faster on 16-channel blocks than split in time.
-  if (N > 16) {
+  // Measured on MI355X: at N = 16 the 64-channel layout is fastest once it
+  // gives 3 waves per SIMD; below that 16-channel blocks win (the cross scan's
+  // 1.5 waves per SIMD: -14 %), split in time when they too are short of
+  // waves (long sequences with few rows), into enough chunks for ~24 waves per
+  // SIMD (32 -> 48 or 64 chunks: -2 to -3 % on the long workloads).  Smaller N
+  // has only the 64-channel layout, larger N only the 16-channel one.
+  const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
+  if (N > 16 || (N == 16 && waves0 < MSCAN_TARGET_WAVES)) {
     layout = 2;
-    const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
-    if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2);
-  } else if (waves0 < MSCAN_TARGET_WAVES / 2) {
-    if (N >= 16 && L < 8 * MSCAN_MIN_CHUNK) {
-      layout = 2;
-      const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
-      if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2);
-    } else if (L >= 2 * MSCAN_MIN_CHUNK) {
-      nch = split(waves0);
-    }
+    if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2, 8 * MSCAN_TARGET_WAVES);
+  } else if (waves0 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) {
+    nch = split(waves0, MSCAN_TARGET_WAVES);
   }
   if ((MSCAN_FORCE_LAYOUT == 0 || MSCAN_FORCE_LAYOUT == 2) && N == 16) layout = MSCAN_FORCE_LAYOUT;
   if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;

@@ -82,9 +82,12 @@ SMALL = {
     "rows768_cross2d_f32": I.Workload("rows768_cross2d_f32", 3, 1024, 36, 16, I.DIR_CROSS2D, "f32", False, 26, 6, 6),
     # enough rows for 64-channel blocks of 4 states per thread
     "wide4_bidir_bf16": I.Workload("wide4_bidir_bf16", 16, 1536, 20, 16, I.DIR_BIDIR, "bf16", True, 27),
-    # few rows, long sequence: 64-channel blocks split in time
+    # few rows, long sequence: 16-channel blocks split in time (N = 16), and
+    # 64-channel blocks split in time (N < 16 has only those)
     "split_long_fwd_bf16": I.Workload("split_long_fwd_bf16", 1, 64, 9000, 16, I.DIR_FWD, "bf16", True, 28),
     "split_long_bidir_f32": I.Workload("split_long_bidir_f32", 1, 64, 8500, 16, I.DIR_BIDIR, "f32", True, 29),
+    "split_long_fwd_bf16_n8": I.Workload("split_long_fwd_bf16_n8", 1, 64, 9000, 8, I.DIR_FWD, "bf16", True, 30),
+    "split_long_bidir_f32_n4": I.Workload("split_long_bidir_f32_n4", 1, 72, 5000, 4, I.DIR_BIDIR, "f32", True, 31),
 }
 
 
