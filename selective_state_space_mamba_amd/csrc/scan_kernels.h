@@ -489,45 +489,53 @@ struct StepParams {
   int Bsz, Dm, softplus;
 };
 
+// One token.  TPC = N/G threads per (batch, channel), each with G <= 4
+// consecutive states (one 16-byte state load and store); the readout is summed
+// over the channel's TPC lanes with xor shuffles and lane 0 of the group adds
+// the skip, gates and stores.  Consecutive threads take consecutive state
+// groups, so the state traffic is coalesced.
 template <typename TIn, int N, bool EXACT>
 __global__ void __launch_bounds__(256) scan_step_kernel(const StepParams p) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= p.Bsz * p.Dm) return;
-  const int b = i / p.Dm, d = i - b * p.Dm;
-  const TIn* Bt = static_cast<const TIn*>(p.B_t) + (int64_t)b * N;
-  const TIn* Ct = static_cast<const TIn*>(p.C_t) + (int64_t)b * N;
+  constexpr int G = N < 4 ? N : 4;  // states per thread
+  constexpr int TPC = N / G;        // threads per channel (a power of two, at most 16)
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = gi / TPC;  // (b, d)
+  const int n0 = (int)(gi % TPC) * G;
+  // (a channel's TPC lanes are all in range or all out: TPC divides the wave)
+  if (i >= (int64_t)p.Bsz * p.Dm) return;
+  const int b = (int)(i / p.Dm), d = (int)(i - (int64_t)b * p.Dm);
   const float x = load1(static_cast<const TIn*>(p.delta_t) + i) + (p.delta_bias ? p.delta_bias[d] : 0.f);
   const float dl = p.softplus ? softplus_log2(x) : x * kLog2e;  // Δ' = Δ·log2 e
   const float uu = load1(static_cast<const TIn*>(p.u_t) + i);
   const float du = dl * uu * kLn2;  // Δ·u
-  float* st = p.state + (int64_t)i * N;
-  const float* Ad = p.A + (int64_t)d * N;
+  float* st = p.state + i * N + n0;
+  const float* Ad = p.A + (int64_t)d * N + n0;
+  Small<float, G> hv, Av;
+  Small<TIn, G> Bs, Cs;
+  hv.load(st);
+  Av.load(Ad);
+  Bs.load(static_cast<const TIn*>(p.B_t) + (int64_t)b * N + n0);
+  Cs.load(static_cast<const TIn*>(p.C_t) + (int64_t)b * N + n0);
+  float hs[G];
   float y = 0.f;
 #pragma unroll
-  for (int n0 = 0; n0 < N; n0 += 4) {
-    constexpr int E = N < 4 ? N : 4;
-    float hs[E];
-    Small<float, E> hv;
-    Small<TIn, E> Bs, Cs;
-    hv.load(st + n0);
-    Bs.load(Bt + n0);
-    Cs.load(Ct + n0);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float An = Ad[n0 + e];
-      const float a = ex2(dl * An);  // e^(Δ·A) = 2^(Δ'·A)
-      float bu = du * Bs.get(e);
-      if constexpr (EXACT) bu = zoh_coef(a, dl * An * kLn2, dl * kLn2, An != 0.f ? 1.0f / An : 0.f) * (uu * Bs.get(e));
-      hs[e] = __builtin_fmaf(a, hv.get(e), bu);
-      y = __builtin_fmaf(Cs.get(e), hs[e], y);
-    }
-    if (E == 4) {
-      *reinterpret_cast<float4*>(st + n0) = make_float4(hs[0], hs[E > 1 ? 1 : 0], hs[E > 2 ? 2 : 0], hs[E > 3 ? 3 : 0]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) st[n0 + e] = hs[e];
-    }
+  for (int e = 0; e < G; ++e) {
+    const float An = Av.get(e);
+    const float a = ex2(dl * An);  // e^(Δ·A) = 2^(Δ'·A)
+    float bu = du * Bs.get(e);
+    if constexpr (EXACT) bu = zoh_coef(a, dl * An * kLn2, dl * kLn2, An != 0.f ? 1.0f / An : 0.f) * (uu * Bs.get(e));
+    hs[e] = __builtin_fmaf(a, hv.get(e), bu);
+    y = __builtin_fmaf(Cs.get(e), hs[e], y);
   }
+  if constexpr (G == 4) {
+    *reinterpret_cast<float4*>(st) = make_float4(hs[0], hs[G > 1 ? 1 : 0], hs[G > 2 ? 2 : 0], hs[G > 3 ? 3 : 0]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < G; ++e) st[e] = hs[e];
+  }
+#pragma unroll
+  for (int m = 1; m < TPC; m <<= 1) y += __shfl_xor(y, m, TPC);
+  if (n0 != 0) return;
   y += (p.D ? p.D[d] : 0.f) * uu;
   if (p.z_t) y *= silu_f(load1(static_cast<const TIn*>(p.z_t) + i));
   store1(static_cast<TIn*>(p.out) + i, y);

@@ -125,7 +125,8 @@ int dispatch_scan(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s)
 
 template <typename TIn, int N, bool EXACT>
 int launch_step(const StepParams& p, hipStream_t stream) {
-  const unsigned blocks = (unsigned)((p.Bsz * p.Dm + 255) / 256);
+  constexpr int TPC = N < 4 ? 1 : N / 4;  // threads per (batch, channel)
+  const unsigned blocks = (unsigned)(((int64_t)p.Bsz * p.Dm * TPC + 255) / 256);
   hipLaunchKernelGGL((scan_step_kernel<TIn, N, EXACT>), dim3(blocks), dim3(256), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }

@@ -256,8 +256,10 @@ def run_decode(w, L0, steps, rows=None, exact_zoh=False):
     tail = {k: to_dev(np.ascontiguousarray(x[k][:, L0:].swapaxes(0, 1))) for k in ("u", "delta", "B", "C", "z")}
     outs = []
     for s in range(steps):
-        outs.append(ms.scan_step(state, tail["u"][s], tail["delta"][s], xd["A"], tail["B"][s],
-                                 tail["C"][s], xd["D"], tail["z"][s], xd["delta_bias"], exact_zoh=exact_zoh))
+        # (fresh allocations: a [B][N] slice of small N is not 16-byte aligned)
+        t = {k: tail[k][s].clone() for k in tail}
+        outs.append(ms.scan_step(state, t["u"], t["delta"], xd["A"], t["B"], t["C"], xd["D"], t["z"],
+                                 xd["delta_bias"], exact_zoh=exact_zoh))
     torch().cuda.synchronize()
     got = np.stack([from_dev(o) for o in outs], axis=1)  # [B][steps][D]
     ref_out, ref_st = oracle_fwd(w.with_(seqlen=L0 + steps), x, rows=rows, exact_zoh=exact_zoh)
@@ -273,6 +275,14 @@ def test_decode_continues_scan_small():
     got, st, ref_out, ref_st = run_decode(wf, 64, 16)
     assert_close("decode f32 out", got, ref_out[:, 64:], "f32")
     assert_close("decode f32 state", st, ref_st[:, 0], "f32")
+
+
+@pytest.mark.parametrize("N", [1, 2, 8, 32, 64])
+def test_decode_state_sizes(N):
+    w = I.Workload("dec_N%d" % N, 2, 40, 0, N, I.DIR_FWD, "f32", True, 54 + N)
+    got, st, ref_out, ref_st = run_decode(w, 50, 12)
+    assert_close("decode N=%d out" % N, got, ref_out[:, 50:], "f32")
+    assert_close("decode N=%d state" % N, st, ref_st[:, 0], "f32")
 
 
 def test_decode_exact_zoh():
