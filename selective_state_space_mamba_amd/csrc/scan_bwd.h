@@ -216,8 +216,12 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
 // pass then starts chunk c from the fold over the later chunks j,
 // carry <- S_j + e^{A·ΣΔ_j}·carry (the carry's dependence on its start value
 // is the product of the chunk's decays).
+// (The exact rule's two coefficient series need more registers than a
+// 2-wave budget: it spilled ~200 bytes per lane and ran 1.7x slower than with
+// the 1-wave budget it gets here.)
 template <typename TIn, int N, bool EXACT, bool AGG>
-__global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), MSCAN_BWD_WAVES) scan_bwd_kernel(const BwdParams p) {
+__global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WAVES)
+    scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
   constexpr int NGP = N < 4 ? 4 : N;  // thread rows
   constexpr int NT = CB * NGP;
