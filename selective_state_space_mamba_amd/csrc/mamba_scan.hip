@@ -310,7 +310,8 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   const bool exact = dims->exact_zoh != 0;
   const int64_t N = dims->dstate;
 
-  // 1. forward recompute: per-direction output rows and state checkpoints
+  // 1. forward recompute: state checkpoints (and, for dz, the per-direction
+  // fp32 output rows)
   ScanParams p{};
   p.u = u;
   p.delta = delta;
@@ -322,7 +323,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   p.delta_bias = delta_bias;
   p.init_state = dims->initial_state;
   p.out = nullptr;
-  p.ws_y = wsf(bp.ws_y);
+  p.ws_y = (z && dz) ? wsf(bp.ws_y) : nullptr;  // the rows serve dz alone
   p.agg_state = pl.agg_state_bytes ? wsf(bp.agg) : nullptr;
   p.agg_dsum = pl.agg_dsum_bytes ? wsf(bp.agg + pl.agg_state_bytes) : nullptr;
   p.last_state = nullptr;

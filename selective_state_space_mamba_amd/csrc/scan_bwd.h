@@ -76,7 +76,8 @@ struct BwdParams {
   const float* ckpt;        // [K][Bsz][ntiles][Dm][N] states at every 32-position tile start
   const void* dout;         // [Bsz][L][Dm]
   const void* z;            // [Bsz][L][Dm] or null (no gate)
-  const float* ws_y;        // [K][Bsz][L][Dm] ungated output rows of the forward recompute
+  const float* ws_y;        // [K][Bsz][L][Dm] ungated output rows of the forward recompute, or null
+                            // (no gate or no dz: not needed)
   void* dz;                 // [Bsz][L][Dm]: written while staging when dz_here
   int dz_here;              // one direction and a gate: dz from this direction's row
   void* du;                 // [Bsz][Ku][L][Dm] (Ku = K), or null when du_part is used
@@ -289,8 +290,8 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WA
   const bool gated = p.z != nullptr;
   const TIn* z_s = gated ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : go_s;  // (no gate: unused loads)
   // the direction's fp32 output row for dz; without dz_here every lane loads
-  // element 0 (one cache line, unused)
-  const float* y_s = p.ws_y + ((int64_t)k * p.Bsz + b) * L * D;
+  // element 0 (one cache line, unused; of dout when there are no rows)
+  const float* y_s = p.ws_y ? p.ws_y + ((int64_t)k * p.Bsz + b) * L * D : static_cast<const float*>(p.dout);
   const int64_t y_mask = p.dz_here ? ~(int64_t)0 : 0;
   const float* ck_s = p.ckpt + ((int64_t)k * p.Bsz + b) * p.ntiles * D * N;
   const bool own = nvalid && dvalid;  // this thread's (channel, state) exists

@@ -60,7 +60,7 @@ struct ScanParams {
   const void* z;            // may be null
   const float* delta_bias;  // may be null
   const float* init_state;  // [Bsz][K][D][N] or null
-  void* out;                // [Bsz][L][D] (single direction)
+  void* out;                // [Bsz][L][D] (single direction), or null with ws_y null: no output
   float* ws_y;              // [K][Bsz][L][D] ungated fp32 rows (several directions) or null
   float* last_state;        // [Bsz][K][D][N] or null
   float* agg_state;         // [K][Bsz][nchunks-1][D][N]
@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
                              : make_rsrc(static_cast<TIn*>(p.out) + (int64_t)b * L * D, slice);
   const TIn* __restrict__ B_base = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* __restrict__ C_base = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
-  const bool gated = !AGG && (p.z != nullptr) && (p.ws_y == nullptr);
+  const bool gated = !AGG && (p.z != nullptr) && (p.ws_y == nullptr) && (p.out != nullptr);
 
   // ---- per-lane constants and the starting state ----
   float Al2[G], h[G], invA[G];
@@ -401,10 +401,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         for (int i = 0; i < TPT; ++i) yv[i] += s_y[g][cl][ng * TPT + i];
       }
       const uint32_t oes = p.ws_y ? 4u : ES;
+      // (no output at all: the recompute of a backward pass that needs only
+      // the state checkpoints)
+      const bool has_out = p.ws_y != nullptr || p.out != nullptr;
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
         const int pp = p0 + ng * TPT + i;
-        if (pp < pend && (dfull || dvalid)) {
+        if (has_out && pp < pend && (dfull || dvalid)) {
           const uint32_t roff = row_elem(pp) * oes;
           const uint32_t soff = CB == 64 ? roff : 0u;
           const uint32_t voff = CB == 64 ? voff_out : voff_out + roff;
