@@ -57,7 +57,7 @@ typedef enum {
                                  the 32-bit offsets used inside one (batch, direction) slice:
                                  (seqlen+64)*dim*sizeof(dtype) below 2^31 bytes, and for
                                  several directions (and for mamba_scan_bwd) seqlen*dim*4
-                                 at most 2^31 bytes */
+                                 at most 2^31 bytes; seqlen and dim*4 below 2^24 */
   MAMBA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mamba_scan_fwd_workspace_bytes() */
   MAMBA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
 } mamba_status;

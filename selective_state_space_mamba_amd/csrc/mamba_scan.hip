@@ -46,6 +46,9 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   if (g->seqlen > INT32_MAX / 2 || g->dim > INT32_MAX / 2 || g->batch > INT32_MAX / 8 ||
       g->batch * g->dim > INT32_MAX / 4)
     return MAMBA_ERR_UNSUPPORTED;
+  // token indices and token-row strides in bytes (up to 4 bytes per element)
+  // are multiplied as 24-bit operands
+  if (g->seqlen >= ((int64_t)1 << 24) || g->dim * 4 >= ((int64_t)1 << 24)) return MAMBA_ERR_UNSUPPORTED;
   // each (batch, direction) slice of L x D elements is addressed through a
   // buffer descriptor with 32-bit offsets (fp32 rows for several directions)
   const int64_t es = g->dtype == MAMBA_DTYPE_BF16 ? 2 : 4;

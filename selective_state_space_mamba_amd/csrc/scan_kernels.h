@@ -232,14 +232,17 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   const uint32_t voff_in = (uint32_t)(d0 + min(cl, dlast)) * ES;
   const uint32_t voff_out = (uint32_t)(d0 + min(cl, dlast)) * (p.ws_y ? 4u : ES);
   const bool dfull = d0 + CB <= D;
-  auto row_elem = [&](int pp) { return (uint32_t)token(min(pp, pend - 1)) * (uint32_t)D; };
+  // Byte offset of the token row of scan position pp (clamped into the chunk)
+  // for a row of D elements of es bytes.  Tokens and row strides are below
+  // 2^24 (checked on the host), so the full-rate 24-bit multiply serves.
+  auto row_off = [&](int pp, uint32_t es) { return __umul24((uint32_t)token(min(pp, pend - 1)), (uint32_t)D * es); };
   // Loads are issued unconditionally (rows clamped into the chunk), so the
   // wait before staging covers exactly the older of the two tiles in flight.
   auto load_tile = [&](int p0, Raw& r) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       // the row offset is a scalar only when the wave's rows are one row (CB = 64)
-      const uint32_t roff = row_elem(p0 + ng * TPT + i) * ES;
+      const uint32_t roff = row_off(p0 + ng * TPT + i, ES);
       const uint32_t soff = CB == 64 ? roff : 0u;
       const uint32_t voff = CB == 64 ? voff_in : voff_in + roff;
       r.dl[i] = buf_load(rs_dl, voff, soff, (TIn*)nullptr);
@@ -250,7 +253,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     for (int i = 0; i < BCI; ++i) {
       const int q = min(tid + i * NT, BCU - 1);
       const int tt = q / UPR, nq = q % UPR;
-      const int64_t off = (int64_t)token(min(p0 + tt, pend - 1)) * N + nq * EQ;
+      const uint32_t off = __umul24((uint32_t)token(min(p0 + tt, pend - 1)), (uint32_t)N) + nq * EQ;
       r.B[i].load(B_base + off);
       if constexpr (!AGG) r.C[i].load(C_base + off);
     }
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       for (int i = 0; i < TPT; ++i) {
         const int pp = p0 + ng * TPT + i;
         if (has_out && pp < pend && (dfull || dvalid)) {
-          const uint32_t roff = row_elem(pp) * oes;
+          const uint32_t roff = row_off(pp, oes);
           const uint32_t soff = CB == 64 ? roff : 0u;
           const uint32_t voff = CB == 64 ? voff_out : voff_out + roff;
           if (p.ws_y) buf_store(yv[i], rs_out, voff, soff);

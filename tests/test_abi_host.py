@@ -95,6 +95,11 @@ def test_fwd_validation(lib):
     lmax = (2**31 - 1) // (dim * 2) - 64
     assert ms.workspace_bytes(dims(batch=1, dim=dim, seqlen=lmax), ms.DIR_FWD) >= 0
     assert call_fwd(lib, dims(batch=1, dim=dim, seqlen=lmax + 1)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    # token indices and row strides are 24-bit multiply operands: seqlen and dim * 4 below 2^24
+    assert ms.workspace_bytes(dims(batch=1, dim=8, seqlen=(1 << 24) - 1), ms.DIR_FWD) >= 0
+    assert call_fwd(lib, dims(batch=1, dim=8, seqlen=1 << 24)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert ms.workspace_bytes(dims(batch=1, dim=(1 << 22) - 8, seqlen=64), ms.DIR_FWD) >= 0
+    assert call_fwd(lib, dims(batch=1, dim=1 << 22, seqlen=64)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(dstate=128)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(dim=60)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert call_fwd(lib, dims(), u=FAKE + 4) == ms._binding.MAMBA_ERR_UNSUPPORTED
