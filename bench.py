@@ -291,13 +291,54 @@ def main():
                 evs[i][1].record(stream)
             torch.cuda.synchronize()
         bwd_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+        # the training pass with a saved forward state: mamba_scan_fwd_save,
+        # then mamba_scan_bwd reading it instead of recomputing the states
+        sbytes = ms.saved_bytes(dims, w.dir_mode, w.gated)
+        saveds = [torch.empty(sbytes, dtype=torch.uint8, device=dev) for _ in sets]
+
+        def fsave(i):
+            s_ = sets[i % len(sets)]
+            ms.scan_fwd_save(s_["u"], s_["delta"], s_["A"], s_["B"], s_["C"], s_["D"], s_["z"], s_["delta_bias"],
+                             dir_mode=w.dir_mode, height=w.height, width=w.width, out=outs[i % len(sets)],
+                             last_state=states[i % len(sets)], workspace=ws, saved=saveds[i % len(sets)],
+                             stream=stream)
+
+        def bsaved(i):
+            s_ = sets[i % len(sets)]
+            return ms.scan_bwd(s_["u"], s_["delta"], s_["A"], s_["B"], s_["C"], s_["D"], s_["z"], s_["delta_bias"],
+                               dout=douts[i % len(sets)], dir_mode=w.dir_mode, height=w.height, width=w.width,
+                               workspace=bws, saved=saveds[i % len(sets)], stream=stream)
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                fsave(i)
+                bsaved(i)
+            torch.cuda.synchronize()
+            fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.bwd_steps)]
+            bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.bwd_steps)]
+            for i in range(args.bwd_steps):
+                fev[i][0].record(stream)
+                fsave(i)
+                fev[i][1].record(stream)
+                bev[i][0].record(stream)
+                bsaved(i)
+                bev[i][1].record(stream)
+            torch.cuda.synchronize()
+        fsave_s = float(np.mean([a.elapsed_time(b) for a, b in fev])) * 1e-3
+        bsaved_s = float(np.mean([a.elapsed_time(b) for a, b in bev])) * 1e-3
         bbytes = bwd_algorithmic_bytes(w)
         bwd = {"op": "mamba_scan_bwd: gradients of u, delta, A, B, C, D, z, delta_bias, initial state",
                "us_per_call": bwd_s * 1e6, "elements_per_s": el / bwd_s, "bound": "alu",
                "peak_elements_per_s": BWD_ALU_PEAK_ELEM, "frac": el / bwd_s / BWD_ALU_PEAK_ELEM,
                "algorithmic_bytes": bbytes, "hbm_gbs": bbytes / bwd_s / 1e9,
-               "workspace_bytes": int(bws.numel())}
-        del bws, douts
+               "workspace_bytes": int(bws.numel()),
+               "saved_state": {"op": "mamba_scan_fwd_save, then mamba_scan_bwd from its saved state (no recompute)",
+                               "bytes": int(sbytes), "fwd_save_us_per_call": fsave_s * 1e6,
+                               "bwd_us_per_call": bsaved_s * 1e6,
+                               "fwd_plus_bwd_us": (fsave_s + bsaved_s) * 1e6,
+                               "fwd_plus_recomputing_bwd_us": (avg_launch_s + bwd_s) * 1e6}}
+        del bws, douts, saveds
 
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4

@@ -183,6 +183,34 @@ MAMBA_API int mamba_conv1d_silu(const void* x, const float* weight, const float*
 MAMBA_API size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_mode);
 
 /*
+ * Bytes of the saved forward state that mamba_scan_fwd_save writes and
+ * mamba_scan_bwd can read in place of its forward recompute: the state before
+ * every 32-position tile, [K][B][ceil(L/32)][D][N] float32, and, when gated is
+ * nonzero (a scan with z whose dz will be asked for), after it (at a 256-byte
+ * aligned offset) the ungated per-direction outputs [K][B][L][D] float32.
+ * A pure function of its arguments; (size_t)-1 when the arguments are invalid
+ * or the backward pass is not built for them (as mamba_scan_bwd_workspace_bytes).
+ */
+MAMBA_API size_t mamba_scan_saved_bytes(const mamba_dims* dims, int dir_mode, int gated);
+
+/*
+ * mamba_scan_fwd that also writes the saved forward state (layout above, with
+ * the rows when z is not NULL) into saved, a device buffer of saved_bytes
+ * owned by the caller, so that the training pass's backward need not recompute
+ * the states [MFS §5 and S4M §2.3 recompute them instead; this trades that
+ * recomputation for the buffer: 151 MB for a batch-8, 2048-token, 1536-channel
+ * layer].  out and last_state are those of mamba_scan_fwd for the same
+ * arguments.  Same errors as mamba_scan_fwd, plus MAMBA_ERR_INVALID for a
+ * NULL saved and MAMBA_ERR_WORKSPACE when saved_bytes is below
+ * mamba_scan_saved_bytes(dims, dir_mode, z != NULL); built for dstate N in
+ * 1..16 like the backward pass.
+ */
+MAMBA_API int mamba_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                                  int dir_mode, void* out, float* last_state, void* saved, size_t saved_bytes,
+                                  hipStream_t stream);
+
+/*
  * Selective-scan backward pass: gradients of a loss with respect to every
  * input of mamba_scan_fwd, given dout = ∂loss/∂out [MFS §5 and S4M §2.3: the
  * training pass keeps only the inputs and recomputes the states].  Same
@@ -207,12 +235,18 @@ MAMBA_API size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_
  * any input or each other.  Built for dstate N in 1..16; N = 32 or 64 gives
  * MAMBA_ERR_UNSUPPORTED.  dims->workspace must hold
  * mamba_scan_bwd_workspace_bytes() bytes; its contents need not be
- * initialised.  Errors as for mamba_scan_fwd.
+ * initialised.  saved: NULL to recompute the forward states, or the buffer
+ * mamba_scan_fwd_save wrote for these same inputs, dims and dir_mode (read
+ * only; with z and dz it must hold the rows); the gradients are then the
+ * same, bit for bit, and the recompute is skipped.  MAMBA_ERR_WORKSPACE when
+ * saved is given with saved_bytes below mamba_scan_saved_bytes(dims, dir_mode,
+ * z && dz) or is not 16-byte aligned.  Other errors as for mamba_scan_fwd.
  */
 MAMBA_API int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                              const float* D, const void* z, const float* delta_bias, const void* dout,
                              const mamba_dims* dims, int dir_mode, void* du, void* ddelta, float* dA, void* dB,
-                             void* dC, float* dD, void* dz, float* ddelta_bias, float* dinit, hipStream_t stream);
+                             void* dC, float* dD, void* dz, float* ddelta_bias, float* dinit, const void* saved,
+                             size_t saved_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 MAMBA_API const char* mamba_status_string(int status);

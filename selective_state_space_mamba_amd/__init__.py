@@ -8,8 +8,8 @@ tests and the benchmark (inputs.py).
 """
 from ._binding import (DIR_BIDIR, DIR_BWD, DIR_CROSS2D, DIR_FWD, DTYPE_BF16, DTYPE_F32, EXPORTED, LIB_PATH,
                        MambaDims, MambaError, bwd_workspace_bytes, conv1d_silu, load_library, make_dims, num_dirs,
-                       scan_bwd, scan_fwd, scan_step, status_string, workspace_bytes)
+                       saved_bytes, scan_bwd, scan_fwd, scan_fwd_save, scan_step, status_string, workspace_bytes)
 
 __all__ = ["DIR_BIDIR", "DIR_BWD", "DIR_CROSS2D", "DIR_FWD", "DTYPE_BF16", "DTYPE_F32", "EXPORTED", "LIB_PATH",
            "MambaDims", "MambaError", "bwd_workspace_bytes", "conv1d_silu", "load_library", "make_dims", "num_dirs",
-           "scan_bwd", "scan_fwd", "scan_step", "status_string", "workspace_bytes"]
+           "saved_bytes", "scan_bwd", "scan_fwd", "scan_fwd_save", "scan_step", "status_string", "workspace_bytes"]

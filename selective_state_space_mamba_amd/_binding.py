@@ -17,7 +17,8 @@ MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_E
 DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTED = ("mamba_conv1d_silu", "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd_workspace_bytes",
-            "mamba_scan_fwd", "mamba_scan_step", "mamba_status_string")
+            "mamba_scan_fwd", "mamba_scan_fwd_save", "mamba_scan_saved_bytes", "mamba_scan_step",
+            "mamba_status_string")
 
 
 class MambaDims(ctypes.Structure):
@@ -64,7 +65,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mamba_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.mamba_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(MambaDims), i32]
     lib.mamba_scan_bwd.restype = i32
-    lib.mamba_scan_bwd.argtypes = [vp] * 9 + [ctypes.POINTER(MambaDims), i32] + [vp] * 9 + [vp]
+    lib.mamba_scan_bwd.argtypes = [vp] * 9 + [ctypes.POINTER(MambaDims), i32] + [vp] * 9 + [vp, ctypes.c_size_t, vp]
+    lib.mamba_scan_saved_bytes.restype = ctypes.c_size_t
+    lib.mamba_scan_saved_bytes.argtypes = [ctypes.POINTER(MambaDims), i32, i32]
+    lib.mamba_scan_fwd_save.restype = i32
+    lib.mamba_scan_fwd_save.argtypes = [vp] * 8 + [ctypes.POINTER(MambaDims), i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.mamba_conv1d_silu.restype = i32
     lib.mamba_conv1d_silu.argtypes = [vp, vp, vp, ctypes.POINTER(MambaDims), i32, i32, vp, vp]
     lib.mamba_status_string.restype = ctypes.c_char_p
@@ -128,6 +133,13 @@ def bwd_workspace_bytes(dims: MambaDims, dir_mode: int) -> int:
     return n
 
 
+def saved_bytes(dims: MambaDims, dir_mode: int, gated: bool) -> int:
+    n = load_library().mamba_scan_saved_bytes(ctypes.byref(dims), int(dir_mode), 1 if gated else 0)
+    if n == ctypes.c_size_t(-1).value:
+        raise MambaError(MAMBA_ERR_UNSUPPORTED, "mamba_scan_saved_bytes")
+    return n
+
+
 def _check(t, name, shape, dtype, device):
     if t is None:
         return
@@ -150,6 +162,25 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
     the cross scan): u [B][K][L][D], delta [B][K][L][D], A [K][D][N],
     B/C [B][K][L][N], D/delta_bias [K][D], z [B][L][D].
     Returns (out [B][L][D], last_state [B][K][D][N] or None)."""
+    out, last_state, _ = _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus,
+                              exact_zoh, initial_state, out, last_state, want_last_state, workspace, stream,
+                              False, None)
+    return out, last_state
+
+
+def scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0, width=0,
+                  delta_softplus=True, exact_zoh=False, initial_state=None, out=None, last_state=None,
+                  want_last_state=True, workspace=None, saved=None, stream=None):
+    """mamba_scan_fwd_save on torch tensors: scan_fwd that also fills the
+    saved forward state for scan_bwd(..., saved=...).  saved: a uint8 device
+    tensor of at least saved_bytes(dims, dir_mode, z is not None) bytes, or
+    None to allocate one.  Returns (out, last_state, saved)."""
+    return _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus, exact_zoh,
+                initial_state, out, last_state, want_last_state, workspace, stream, True, saved)
+
+
+def _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus, exact_zoh, initial_state,
+         out, last_state, want_last_state, workspace, stream, save, saved):
     import torch
     lib = load_library()
     K = num_dirs(dir_mode)
@@ -183,21 +214,32 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         dims.workspace = workspace.data_ptr()
         dims.workspace_bytes = workspace.numel() * workspace.element_size()
-    rc = lib.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                            ctypes.byref(dims), int(dir_mode), _ptr(out), _ptr(last_state), _stream(stream))
+    if not save:
+        rc = lib.mamba_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), ctypes.byref(dims), int(dir_mode), _ptr(out), _ptr(last_state),
+                                _stream(stream))
+        if rc != MAMBA_OK:
+            raise MambaError(rc, "mamba_scan_fwd")
+        return out, last_state, None
+    if saved is None:
+        saved = torch.empty(saved_bytes(dims, dir_mode, z is not None), dtype=torch.uint8, device=dev)
+    rc = lib.mamba_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(delta_bias), ctypes.byref(dims), int(dir_mode), _ptr(out), _ptr(last_state),
+                                 _ptr(saved), saved.numel() * saved.element_size(), _stream(stream))
     if rc != MAMBA_OK:
-        raise MambaError(rc, "mamba_scan_fwd")
-    return out, last_state
+        raise MambaError(rc, "mamba_scan_fwd_save")
+    return out, last_state, saved
 
 
 def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dout, dir_mode=DIR_FWD, height=0, width=0,
              delta_softplus=True, exact_zoh=False, initial_state=None, want_dinit=True, workspace=None,
-             stream=None):
+             saved=None, stream=None):
     """mamba_scan_bwd on torch tensors: gradients of sum(dout * out) for the
     scan_fwd call with the same arguments.  Returns a dict with du, ddelta,
     dA, dB, dC (shaped like their inputs), dD and ddelta_bias (None when D or
     delta_bias is None), dz (None without z) and dinit ([B][K][D][N] float32,
-    None unless want_dinit)."""
+    None unless want_dinit).  saved: the buffer scan_fwd_save returned for
+    the same arguments (the forward recompute is then skipped), or None."""
     import torch
     lib = load_library()
     K = num_dirs(dir_mode)
@@ -233,7 +275,8 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dout, dir_mo
     rc = lib.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                             _ptr(dout), ctypes.byref(dims), int(dir_mode), _ptr(g["du"]), _ptr(g["ddelta"]),
                             _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                            _ptr(g["ddelta_bias"]), _ptr(g["dinit"]), _stream(stream))
+                            _ptr(g["ddelta_bias"]), _ptr(g["dinit"]), _ptr(saved),
+                            0 if saved is None else saved.numel() * saved.element_size(), _stream(stream))
     if rc != MAMBA_OK:
         raise MambaError(rc, "mamba_scan_bwd")
     return g

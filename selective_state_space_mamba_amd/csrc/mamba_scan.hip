@@ -226,6 +226,64 @@ int dispatch_conv(int width, const ConvParams& p, hipStream_t stream) {
   }
 }
 
+// ScanParams of a forward pass over these dims (the output, workspace and
+// checkpoint pointers are set by the caller).
+ScanParams scan_params(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                       const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                       int dir_mode, const Plan& pl) {
+  ScanParams p{};
+  p.u = u;
+  p.delta = delta;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.D = D;
+  p.z = z;
+  p.delta_bias = delta_bias;
+  p.init_state = dims->initial_state;
+  p.Bsz = (int)dims->batch;
+  p.Dm = (int)dims->dim;
+  p.L = (int)dims->seqlen;
+  p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
+  p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
+  p.K = pl.K;
+  p.Ku = pl.Ku;
+  p.kinds = kinds_of(dir_mode);
+  p.nchunks = pl.nchunks;
+  p.chunk_len = pl.chunk_len;
+  p.nblk_d = pl.nblk_d;
+  p.softplus = dims->delta_softplus ? 1 : 0;
+  return p;
+}
+
+int dispatch_fwd(const mamba_dims* dims, const ScanParams& p, const Plan& pl, hipStream_t stream) {
+  const bool exact = dims->exact_zoh != 0;
+  if (dims->dtype == MAMBA_DTYPE_BF16)
+    return exact ? dispatch_scan_bf16_exact(dims->dstate, p, pl, stream)
+                 : dispatch_scan_bf16_simple(dims->dstate, p, pl, stream);
+  return exact ? dispatch_scan_f32_exact(dims->dstate, p, pl, stream)
+               : dispatch_scan_f32_simple(dims->dstate, p, pl, stream);
+}
+
+// Saved forward state (mamba_scan_fwd_save -> mamba_scan_bwd): the state
+// before every 32-position tile, [K][B][ceil(L/32)][D][N] fp32, then, for a
+// gated scan, the ungated per-direction rows [K][B][L][D] fp32 (dz needs them).
+struct SavedLayout {
+  BwdPlan bp;
+  size_t rows, total;
+};
+
+int saved_layout(const mamba_dims* g, int mode, bool rows, SavedLayout* s) {
+  const int rc = make_bwd_plan(g, mode, &s->bp);
+  if (rc != MAMBA_OK) return rc;
+  const size_t f4 = sizeof(float);
+  const int64_t K = s->bp.fwd.K;
+  const size_t ck = ((size_t)K * g->batch * s->bp.ntiles * g->dim * g->dstate * f4 + 255) / 256 * 256;
+  s->rows = ck;
+  s->total = ck + (rows ? (size_t)K * g->batch * g->seqlen * g->dim * f4 : 0);
+  return MAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -250,40 +308,52 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
   if (need > 0 && (!dims->workspace || dims->workspace_bytes < need || !aligned16(dims->workspace)))
     return MAMBA_ERR_WORKSPACE;
 
-  ScanParams p{};
-  p.u = u;
-  p.delta = delta;
-  p.A = A;
-  p.B = B;
-  p.C = C;
-  p.D = D;
-  p.z = z;
-  p.delta_bias = delta_bias;
-  p.init_state = dims->initial_state;
+  ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
   p.out = out;
   char* ws = static_cast<char*>(dims->workspace);
   p.ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
   p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
   p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
   p.last_state = last_state;
-  p.Bsz = (int)dims->batch;
-  p.Dm = (int)dims->dim;
-  p.L = (int)dims->seqlen;
-  p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
-  p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
-  p.K = pl.K;
-  p.Ku = pl.Ku;
-  p.kinds = kinds_of(dir_mode);
-  p.nchunks = pl.nchunks;
-  p.chunk_len = pl.chunk_len;
-  p.nblk_d = pl.nblk_d;
-  p.softplus = dims->delta_softplus ? 1 : 0;
-  const bool exact = dims->exact_zoh != 0;
-  if (dims->dtype == MAMBA_DTYPE_BF16)
-    return exact ? dispatch_scan_bf16_exact(dims->dstate, p, pl, stream)
-                 : dispatch_scan_bf16_simple(dims->dstate, p, pl, stream);
-  return exact ? dispatch_scan_f32_exact(dims->dstate, p, pl, stream)
-               : dispatch_scan_f32_simple(dims->dstate, p, pl, stream);
+  return dispatch_fwd(dims, p, pl, stream);
+}
+
+size_t mamba_scan_saved_bytes(const mamba_dims* dims, int dir_mode, int gated) {
+  SavedLayout sl;
+  if (saved_layout(dims, dir_mode, gated != 0, &sl) != MAMBA_OK) return (size_t)-1;
+  return sl.total;
+}
+
+int mamba_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                        int dir_mode, void* out, float* last_state, void* saved, size_t saved_bytes,
+                        hipStream_t stream) {
+  SavedLayout sl;
+  int rc = saved_layout(dims, dir_mode, z != nullptr, &sl);
+  if (rc != MAMBA_OK) return rc;
+  const Plan& pl = sl.bp.fwd;
+  if (!u || !delta || !A || !B || !C || !out || !saved) return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, out, last_state, dims->initial_state, saved};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
+  if (saved_bytes < sl.total) return MAMBA_ERR_WORKSPACE;
+  const size_t need = pl.total();
+  if (need > 0 && (!dims->workspace || dims->workspace_bytes < need || !aligned16(dims->workspace)))
+    return MAMBA_ERR_WORKSPACE;
+
+  ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
+  p.out = out;
+  char* ws = static_cast<char*>(dims->workspace);
+  char* sv = static_cast<char*>(saved);
+  // gated: the per-direction rows go to the saved buffer (the merge reads
+  // them there); ungated with several directions: to the workspace as usual
+  p.ws_y = z ? reinterpret_cast<float*>(sv + sl.rows) : (pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr);
+  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
+  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
+  p.last_state = last_state;
+  p.ckpt = reinterpret_cast<float*>(sv);
+  p.ckpt_tiles = sl.bp.ntiles;
+  return dispatch_fwd(dims, p, pl, stream);
 }
 
 size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_mode) {
@@ -295,10 +365,13 @@ size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_mode) {
 int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const void* dout,
                    const mamba_dims* dims, int dir_mode, void* du, void* ddelta, float* dA, void* dB, void* dC,
-                   float* dD, void* dz, float* ddelta_bias, float* dinit, hipStream_t stream) {
-  BwdPlan bp;
-  int rc = make_bwd_plan(dims, dir_mode, &bp);
+                   float* dD, void* dz, float* ddelta_bias, float* dinit, const void* saved,
+                   size_t saved_bytes, hipStream_t stream) {
+  SavedLayout sl;
+  int rc = saved_layout(dims, dir_mode, z && dz, &sl);
   if (rc != MAMBA_OK) return rc;
+  const BwdPlan& bp = sl.bp;
+  if (saved && (saved_bytes < sl.total || !aligned16(saved))) return MAMBA_ERR_WORKSPACE;
   if (!u || !delta || !A || !B || !C || !dout || !du || !ddelta || !dA || !dB || !dC) return MAMBA_ERR_INVALID;
   const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, dout, du, ddelta, dA, dB, dC, dD, dz,
                         ddelta_bias, dinit, dims->initial_state};
@@ -313,40 +386,23 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   const bool exact = dims->exact_zoh != 0;
   const int64_t N = dims->dstate;
 
-  // 1. forward recompute: state checkpoints (and, for dz, the per-direction
-  // fp32 output rows)
-  ScanParams p{};
-  p.u = u;
-  p.delta = delta;
-  p.A = A;
-  p.B = B;
-  p.C = C;
-  p.D = D;
-  p.z = z;
-  p.delta_bias = delta_bias;
-  p.init_state = dims->initial_state;
-  p.out = nullptr;
-  p.ws_y = (z && dz) ? wsf(bp.ws_y) : nullptr;  // the rows serve dz alone
-  p.agg_state = pl.agg_state_bytes ? wsf(bp.agg) : nullptr;
-  p.agg_dsum = pl.agg_dsum_bytes ? wsf(bp.agg + pl.agg_state_bytes) : nullptr;
-  p.last_state = nullptr;
-  p.ckpt = wsf(bp.ckpt);
-  p.ckpt_tiles = bp.ntiles;
-  p.Bsz = (int)dims->batch;
-  p.Dm = (int)dims->dim;
-  p.L = (int)dims->seqlen;
-  p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
-  p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
-  p.K = pl.K;
-  p.Ku = pl.Ku;
-  p.kinds = kinds_of(dir_mode);
-  p.nchunks = pl.nchunks;
-  p.chunk_len = pl.chunk_len;
-  p.nblk_d = pl.nblk_d;
-  p.softplus = dims->delta_softplus ? 1 : 0;
-  rc = bf16 ? (exact ? dispatch_scan_bf16_exact(N, p, pl, stream) : dispatch_scan_bf16_simple(N, p, pl, stream))
-            : (exact ? dispatch_scan_f32_exact(N, p, pl, stream) : dispatch_scan_f32_simple(N, p, pl, stream));
-  if (rc != MAMBA_OK) return rc;
+  // 1. state checkpoints (and, for dz, the per-direction fp32 output rows):
+  // from the saved forward state, else by a forward recompute
+  ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
+  if (saved) {
+    p.ckpt = reinterpret_cast<float*>(const_cast<void*>(saved));
+    p.ws_y = (z && dz) ? reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(saved)) + sl.rows) : nullptr;
+  } else {
+    p.out = nullptr;
+    p.ws_y = (z && dz) ? wsf(bp.ws_y) : nullptr;  // the rows serve dz alone
+    p.agg_state = pl.agg_state_bytes ? wsf(bp.agg) : nullptr;
+    p.agg_dsum = pl.agg_dsum_bytes ? wsf(bp.agg + pl.agg_state_bytes) : nullptr;
+    p.last_state = nullptr;
+    p.ckpt = wsf(bp.ckpt);
+    p.ckpt_tiles = bp.ntiles;
+    rc = dispatch_fwd(dims, p, pl, stream);
+    if (rc != MAMBA_OK) return rc;
+  }
 
   // 2. dz of several directions (it needs their sum; with one direction the
   // reverse sweep writes dz while staging)

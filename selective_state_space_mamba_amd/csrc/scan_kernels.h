@@ -60,8 +60,10 @@ struct ScanParams {
   const void* z;            // may be null
   const float* delta_bias;  // may be null
   const float* init_state;  // [Bsz][K][D][N] or null
-  void* out;                // [Bsz][L][D] (single direction), or null with ws_y null: no output
-  float* ws_y;              // [K][Bsz][L][D] ungated fp32 rows (several directions) or null
+  void* out;                // [Bsz][L][D]: written here with one direction (K = 1), else by the
+                            // direction merge; null: no output row
+  float* ws_y;              // [K][Bsz][L][D] ungated fp32 rows (several directions; with one
+                            // direction, kept for the backward pass) or null
   float* last_state;        // [Bsz][K][D][N] or null
   float* agg_state;         // [K][Bsz][nchunks-1][D][N]
   float* agg_dsum;          // [K][Bsz][nchunks-1][D]
@@ -159,11 +161,15 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   const auto rs_u = make_rsrc(u_slice, slice);
   const auto rs_dl = make_rsrc(dl_slice, slice);
   const auto rs_z = make_rsrc(p.z ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : nullptr, p.z ? slice : 0u);
-  const auto rs_out = p.ws_y ? make_rsrc(p.ws_y + ((int64_t)k * p.Bsz + b) * L * D, (uint32_t)((int64_t)L * D * 4))
-                             : make_rsrc(static_cast<TIn*>(p.out) + (int64_t)b * L * D, slice);
+  // the gated output row is written here only with one direction; the
+  // ungated fp32 rows whenever ws_y is given
+  const bool direct = !AGG && p.out != nullptr && p.K == 1;
+  const auto rs_ws = make_rsrc(p.ws_y ? p.ws_y + ((int64_t)k * p.Bsz + b) * L * D : nullptr,
+                               p.ws_y ? (uint32_t)((int64_t)L * D * 4) : 0u);
+  const auto rs_out = make_rsrc(direct ? static_cast<TIn*>(p.out) + (int64_t)b * L * D : nullptr, direct ? slice : 0u);
   const TIn* __restrict__ B_base = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* __restrict__ C_base = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
-  const bool gated = !AGG && (p.z != nullptr) && (p.ws_y == nullptr) && (p.out != nullptr);
+  const bool gated = direct && p.z != nullptr;
 
   // ---- per-lane constants and the starting state ----
   float Al2[G], h[G], invA[G];
@@ -230,7 +236,8 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // at staging and never stored).
   const int dlast = D - 1 - d0;
   const uint32_t voff_in = (uint32_t)(d0 + min(cl, dlast)) * ES;
-  const uint32_t voff_out = (uint32_t)(d0 + min(cl, dlast)) * (p.ws_y ? 4u : ES);
+  const uint32_t voff_ws = (uint32_t)(d0 + min(cl, dlast)) * 4u;
+  const uint32_t voff_out = (uint32_t)(d0 + min(cl, dlast)) * ES;
   const bool dfull = d0 + CB <= D;
   // Byte offset of the token row of scan position pp (clamped into the chunk)
   // for a row of D elements of es bytes.  Tokens and row strides are below
@@ -403,19 +410,21 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
 #pragma unroll
         for (int i = 0; i < TPT; ++i) yv[i] += s_y[g][cl][ng * TPT + i];
       }
-      const uint32_t oes = p.ws_y ? 4u : ES;
-      // (no output at all: the recompute of a backward pass that needs only
-      // the state checkpoints)
-      const bool has_out = p.ws_y != nullptr || p.out != nullptr;
+      // (neither row: the recompute of a backward pass that needs only the
+      // state checkpoints)
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
         const int pp = p0 + ng * TPT + i;
-        if (has_out && pp < pend && (dfull || dvalid)) {
-          const uint32_t roff = row_off(pp, oes);
-          const uint32_t soff = CB == 64 ? roff : 0u;
-          const uint32_t voff = CB == 64 ? voff_out : voff_out + roff;
-          if (p.ws_y) buf_store(yv[i], rs_out, voff, soff);
-          else store_out(gated ? yv[i] * gate[i] : yv[i], rs_out, voff, soff, (TIn*)nullptr);
+        if (pp < pend && (dfull || dvalid)) {
+          if (p.ws_y) {
+            const uint32_t roff = row_off(pp, 4u);
+            buf_store(yv[i], rs_ws, CB == 64 ? voff_ws : voff_ws + roff, CB == 64 ? roff : 0u);
+          }
+          if (direct) {
+            const uint32_t roff = row_off(pp, ES);
+            store_out(gated ? yv[i] * gate[i] : yv[i], rs_out, CB == 64 ? voff_out : voff_out + roff,
+                      CB == 64 ? roff : 0u, (TIn*)nullptr);
+          }
         }
       }
     }

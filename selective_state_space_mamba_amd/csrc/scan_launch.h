@@ -98,7 +98,7 @@ int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
     rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
   }
   if (rc != MAMBA_OK) return rc;
-  if (p.ws_y && p.out) {  // (the backward pass keeps only the per-direction rows)
+  if (p.ws_y && p.out && p.K > 1) {  // (with one direction the scan wrote out itself)
     const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
     const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
     hipLaunchKernelGGL((merge_dirs_kernel<TIn>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,

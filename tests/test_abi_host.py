@@ -155,11 +155,12 @@ def test_bwd_workspace_and_validation(lib):
 
     def bwd(dd, mode=ms.DIR_FWD, **ptrs):
         p = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, dout=FAKE, du=FAKE,
-                 ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dinit=None)
+                 ddelta=FAKE, dA=FAKE, dB=FAKE, dC=FAKE, dD=None, dz=None, dbias=None, dinit=None, saved=None,
+                 saved_bytes=0)
         p.update(ptrs)
         return lib.mamba_scan_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"], p["dout"],
                                   ctypes.byref(dd), mode, p["du"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"],
-                                  p["dz"], p["dbias"], p["dinit"], None)
+                                  p["dz"], p["dbias"], p["dinit"], p["saved"], p["saved_bytes"], None)
     E = ms._binding
     assert bwd(d, dout=None) == E.MAMBA_ERR_INVALID
     assert bwd(d, dB=None) == E.MAMBA_ERR_INVALID
@@ -169,3 +170,40 @@ def test_bwd_workspace_and_validation(lib):
     assert bwd(d, dz=FAKE + 2) == E.MAMBA_ERR_UNSUPPORTED
     assert bwd(d) == E.MAMBA_ERR_WORKSPACE  # the backward pass always needs its workspace
     assert bwd(dims(workspace=FAKE, workspace_bytes=need - 256)) == E.MAMBA_ERR_WORKSPACE
+    # a saved forward state too small for the call (with z and dz it must hold the rows), or misaligned
+    ws = dict(workspace=FAKE, workspace_bytes=need)
+    ck = ms.saved_bytes(d, ms.DIR_FWD, False)
+    assert bwd(dims(**ws), saved=FAKE, saved_bytes=ck - 4) == E.MAMBA_ERR_WORKSPACE
+    assert bwd(dims(**ws), saved=FAKE, saved_bytes=ck, z=FAKE, dz=FAKE) == E.MAMBA_ERR_WORKSPACE
+    assert bwd(dims(**ws), saved=FAKE + 8, saved_bytes=10 * ck) == E.MAMBA_ERR_WORKSPACE
+
+
+def test_saved_state_size_and_fwd_save_validation(lib):
+    L, Dm, N, Bz = 100, 64, 16, 2
+    d = dims()
+    ck = ms.saved_bytes(d, ms.DIR_FWD, False)
+    # the state before each of the ceil(L/32) tiles, 256-byte aligned, then the fp32 output rows
+    assert ck == (Bz * 4 * Dm * N * 4 + 255) // 256 * 256
+    assert ms.saved_bytes(d, ms.DIR_FWD, True) == ck + Bz * L * Dm * 4
+    cross = dims(seqlen=96, height=8, width=12)
+    assert ms.saved_bytes(cross, ms.DIR_CROSS2D, True) == 4 * Bz * 3 * Dm * N * 4 + 4 * Bz * 96 * Dm * 4
+    for bad in (dims(dstate=32), dims(seqlen=0), dims(dim=60)):
+        with pytest.raises(ms.MambaError):
+            ms.saved_bytes(bad, ms.DIR_FWD, False)
+
+    def fwd_save(dd, mode=ms.DIR_FWD, **ptrs):
+        p = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, out=FAKE, last=None,
+                 saved=FAKE, saved_bytes=ck)
+        p.update(ptrs)
+        return lib.mamba_scan_fwd_save(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"],
+                                       ctypes.byref(dd), mode, p["out"], p["last"], p["saved"], p["saved_bytes"],
+                                       None)
+    E = ms._binding
+    assert fwd_save(d, saved=None) == E.MAMBA_ERR_INVALID
+    assert fwd_save(d, out=None) == E.MAMBA_ERR_INVALID
+    assert fwd_save(dims(batch=0)) == E.MAMBA_ERR_INVALID
+    assert fwd_save(dims(dstate=32)) == E.MAMBA_ERR_UNSUPPORTED  # what the backward pass cannot read
+    assert fwd_save(d, saved=FAKE + 4) == E.MAMBA_ERR_UNSUPPORTED
+    assert fwd_save(d, saved_bytes=ck - 1) == E.MAMBA_ERR_WORKSPACE
+    assert fwd_save(d, z=FAKE) == E.MAMBA_ERR_WORKSPACE  # with a gate the rows are saved too
+    assert fwd_save(d, mode=ms.DIR_BIDIR, saved_bytes=10 ** 9) == E.MAMBA_ERR_WORKSPACE  # the forward's own

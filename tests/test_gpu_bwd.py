@@ -103,10 +103,8 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
-def test_bwd_small(case):
+def small_inputs(case):
     name, w, softplus, exact, with_init, skip = case
-    announce("bwd %s %s softplus=%s exact=%s init=%s" % (name, w, softplus, exact, with_init))
     x = I.make_inputs(w)
     if not skip:
         x["D"] = None
@@ -119,6 +117,14 @@ def test_bwd_small(case):
             x["delta_bias"] = r.uniform(0.0, 0.05, x["delta_bias"].shape).astype(np.float32)
     dout = I.make_dout(w)
     init = init_state(w, w.seed) if with_init else None
+    return x, dout, init
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_bwd_small(case):
+    name, w, softplus, exact, with_init, skip = case
+    announce("bwd %s %s softplus=%s exact=%s init=%s" % (name, w, softplus, exact, with_init))
+    x, dout, init = small_inputs(case)
     got = gpu_bwd(w, x, dout, softplus=softplus, exact=exact, init=init)
     ref = oracle_bwd(w, x, dout, softplus=softplus, exact=exact, init=init)
     compare(name, w, got, ref)
@@ -160,11 +166,52 @@ def test_bwd_optional_outputs_absent():
     rc = lib.mamba_scan_bwd(p(xd["u"]), p(xd["delta"]), p(xd["A"]), p(xd["B"]), p(xd["C"]), p(xd["D"]), p(xd["z"]),
                             p(xd["delta_bias"]), p(dout), ctypes.byref(dims), w.dir_mode, p(part["du"]),
                             p(part["ddelta"]), p(part["dA"]), p(part["dB"]), p(part["dC"]), None, None, None, None,
-                            t.cuda.current_stream().cuda_stream)
+                            None, 0, t.cuda.current_stream().cuda_stream)
     assert rc == 0
     t.cuda.synchronize()
     for k in part:
         assert t.equal(part[k], full[k]), k
+
+
+def saved_vs_recompute(name, w, xd, dout, init=None, softplus=True, exact=False):
+    """mamba_scan_fwd_save returns mamba_scan_fwd's out and last_state, and the
+    backward from its saved state equals the recomputing backward bit for bit
+    (both take the same states from the same forward plan)."""
+    t = torch()
+    kw = dict(dir_mode=w.dir_mode, height=w.height, width=w.width, delta_softplus=softplus, exact_zoh=exact,
+              initial_state=init)
+    args = (xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd.get("D"), xd.get("z"), xd.get("delta_bias"))
+    out0, st0 = ms.scan_fwd(*args, **kw)
+    out1, st1, saved = ms.scan_fwd_save(*args, **kw)
+    g0 = ms.scan_bwd(*args, dout=dout, **kw)
+    g1 = ms.scan_bwd(*args, dout=dout, saved=saved, **kw)
+    t.cuda.synchronize()
+    assert t.equal(out0, out1), name + " out"
+    assert t.equal(st0, st1), name + " last_state"
+    for k in g0:
+        assert (g0[k] is None) == (g1[k] is None), k
+        if g0[k] is not None:
+            assert t.equal(g0[k], g1[k]), "%s %s" % (name, k)
+
+
+SAVED = [c for c in SMALL if c[0] in ("fwd_bf16", "fwd_f32_n4_exact_init", "bwd_bf16_n8", "bidir_f32_init",
+                                      "cross2d_bf16", "cross2d_f32_n1_gated", "split_fwd_bf16", "split_bidir_f32",
+                                      "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16")]
+
+
+@pytest.mark.parametrize("case", SAVED, ids=[c[0] for c in SAVED])
+def test_saved_state_small(case):
+    name, w, softplus, exact, with_init, skip = case
+    announce("saved %s %s" % (name, w))
+    x, dout, init = small_inputs(case)
+    saved_vs_recompute(name, w, dev_inputs(x), to_dev(dout), to_dev(init), softplus, exact)
+
+
+@pytest.mark.parametrize("wname", ["mamba130m_layer", "vmamba_ss2d"])
+def test_saved_state_full_size(wname):
+    w = I.WORKLOADS[wname]
+    announce("saved full %s" % (w,))
+    saved_vs_recompute(wname, w, dev_inputs(I.make_inputs(w)), to_dev(I.make_dout(w)))
 
 
 # (workload, check whole batch items): the 97k-token Vim image has one batch
