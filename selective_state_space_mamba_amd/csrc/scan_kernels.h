@@ -352,11 +352,11 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-          a[r][j] = ex2(o.dl[r] * Al2[j]);
+          const float t = o.dl[r] * Al2[j];  // Δ'·A = ΔA / ln 2
+          a[r][j] = ex2(t);
           if constexpr (EXACT) {
-            // (e^{ΔA} - 1)/A · B·u; Δ'·A·ln 2 = ΔA, Δ'·ln 2 = Δ
-            const float x = o.dl[r] * Al2[j] * kLn2;
-            bu[r][j] = zoh_coef(a[r][j], x, o.dl[r] * kLn2, invA[j]) * (o.du[r] * o.B[j][r]);
+            // (e^{ΔA} - 1)/A · B·u
+            bu[r][j] = zoh_coef_b2(a[r][j], t, o.dl[r], invA[j]) * (o.du[r] * o.B[j][r]);
           } else {
             bu[r][j] = o.du[r] * o.B[j][r];
           }
