@@ -239,7 +239,25 @@ def main():
                 ms.scan_step(st, ut, dt_, s0["A"], Bt, Ct, s0["D"], zt, s0["delta_bias"], out=o, stream=stream)
             torch.cuda.synchronize()
             dec_s = time.perf_counter() - t0
+        # the same loop captured once as a HIP graph and replayed (no host
+        # work per step): the kernel-bound rate of the decode loop
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cs):
+            for _ in range(args.decode_steps):
+                ms.scan_step(st, ut, dt_, s0["A"], Bt, Ct, s0["D"], zt, s0["delta_bias"], out=o, stream=cs)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        gdec_s = time.perf_counter() - t0
+        del graph
         decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
+                  "graph_us_per_step": gdec_s * 1e6 / args.decode_steps,
                   "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4}
 
     conv = None
@@ -370,6 +388,8 @@ def main():
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)",
                      "traffic_gbs": (traffic / avg_launch_s / 1e9) if traffic else None,
                      "kernel_avg_us": avg_launch_s * 1e6,
+                     "kernel_median_us": float(np.median(launch_ms)) * 1e3,
+                     "kernel_min_us": float(np.min(launch_ms)) * 1e3,
                      "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
                              "algorithmic_bytes": alg_bytes}},
         "cpu_baseline": cpu,
