@@ -171,8 +171,8 @@ def main():
                          "MIB-MiB buffer (known bytes, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the scan has no multi-GPU path in this build "
-              "(rows shard across GPUs with no communication; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU: the scan library has no multi-GPU path (its (direction, "
+              "batch, channel) rows would shard across GPUs with no communication)", file=sys.stderr)
         sys.exit(2)
 
     import torch

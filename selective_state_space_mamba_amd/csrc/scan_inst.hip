@@ -1,5 +1,6 @@
 // scan_inst.hip -- kernel instantiations and dispatchers for one element type
-// and one input-term rule, selected by the build:
+// and one input-term rule, selected by compile definitions (build.py compiles this
+// file four times):
 //   MSCAN_INST_BF16  = 1 (bfloat16 tensors) or 0 (float32)
 //   MSCAN_INST_EXACT = 1 (exact zero-order hold) or 0 (Δ·B·u)
 #define MSCAN_INSTANTIATE
