@@ -61,35 +61,27 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
   // Layout and time split.  Waves wanted: MSCAN_TARGET_WAVES (3 per SIMD),
   // since one wave alone issues vector instructions at about half the SIMD rate.
+  // Measured on MI355X: at N = 16 the 16-channel blocks beat the 64-channel
+  // ones at every size tried once the wave priorities were in (Vim-224
+  // 239 -> 219 µs, a batch-32 130M-shaped layer 646 -> 491 µs), so N >= 16
+  // always uses them; smaller N has only the 64-channel layout.  Rows short of
+  // waves (long sequences with few rows) are split in time, the 16-channel
+  // layout into enough chunks for ~24 waves per SIMD (32 -> 48 or 64 chunks:
+  // -2 to -3 % on the long workloads).
   const int64_t L = g->seqlen;
-  const int64_t rows64 = (int64_t)K * g->batch * ((g->dim + 63) / 64);
-  const int64_t waves0 = rows64 * (threads_of((int)N, 0) / 64);
-  int layout = 0;
+  const int cb = layout_of((int)N).cb;
+  const int64_t waves = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb) * (threads_of((int)N) / 64);
   int64_t nch = 1;
-  auto split = [&](int64_t waves, int64_t target) {
+  auto split = [&](int64_t target) {
     int64_t c = (target + waves - 1) / waves;
     if (c > L / MSCAN_MIN_CHUNK) c = L / MSCAN_MIN_CHUNK;
     if (c > MSCAN_MAX_CHUNKS) c = MSCAN_MAX_CHUNKS;
     return c < 1 ? (int64_t)1 : c;
   };
-  // Measured on MI355X: at N = 16 the 64-channel layout is fastest once it
-  // gives 3 waves per SIMD; below that 16-channel blocks win (the cross scan's
-  // 1.5 waves per SIMD: -14 %), split in time when they too are short of
-  // waves (long sequences with few rows), into enough chunks for ~24 waves per
-  // SIMD (32 -> 48 or 64 chunks: -2 to -3 % on the long workloads).  Smaller N
-  // has only the 64-channel layout, larger N only the 16-channel one.
-  const int64_t waves2 = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (threads_of((int)N, 2) / 64);
-  if (N > 16 || (N == 16 && waves0 < MSCAN_TARGET_WAVES)) {
-    layout = 2;
-    if (waves2 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) nch = split(waves2, 8 * MSCAN_TARGET_WAVES);
-  } else if (waves0 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK) {
-    nch = split(waves0, MSCAN_TARGET_WAVES);
-  }
-  if ((MSCAN_FORCE_LAYOUT == 0 || MSCAN_FORCE_LAYOUT == 2) && N == 16) layout = MSCAN_FORCE_LAYOUT;
+  if (waves < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK)
+    nch = split(cb == 16 ? 8 * MSCAN_TARGET_WAVES : MSCAN_TARGET_WAVES);
   if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
   if (nch < 1) nch = 1;
-  const int cb = layout_of((int)N, layout).cb;
-  pl->layout = layout;
   pl->cb = cb;
   pl->nblk_d = (int)((g->dim + cb - 1) / cb);
   int64_t clen = (L + nch - 1) / nch;

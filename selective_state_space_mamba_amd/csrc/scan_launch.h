@@ -22,9 +22,6 @@ inline constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 #ifndef MSCAN_TARGET_WAVES
 #define MSCAN_TARGET_WAVES 3072  // resident waves wanted: 3 per SIMD (one wave issues VALU at half rate)
 #endif
-#ifndef MSCAN_FORCE_LAYOUT
-#define MSCAN_FORCE_LAYOUT -1
-#endif
 #ifndef MSCAN_FORCE_CHUNKS
 #define MSCAN_FORCE_CHUNKS 0
 #endif
@@ -36,22 +33,19 @@ inline constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 #endif
 
 // Workgroup layouts: CB channels per workgroup, G states per thread,
-// CB*N/G threads.  Layout 0 (64 channels, N/4 states per thread, 4 waves) is
-// the cheapest per element: the readout sums 4 partials per (token, channel)
-// and each wave's B, C reads are wave-uniform.  Layout 2 uses 16-channel
-// blocks with N/16 states per thread to spread few rows over every CU, at a
-// higher LDS cost per element.  State sizes below 16 use layout 0 only, state
-// sizes above 16 layout 2 only (at most 4 states per thread).
+// CB*N/G threads.  State sizes below 16 use 64-channel blocks with up to 4
+// states per thread (the readout sums N/G partials per (token, channel) and
+// each wave's B, C reads are wave-uniform); state sizes of 16 and above use
+// 16-channel blocks with N/16 states per thread (at most 4), whose waves
+// hold 4 state rows of the same 16 channels.
 struct Layout {
   int cb, g;
 };
-inline constexpr Layout layout_of(int N, int id) {
-  return N < 16 ? Layout{64, N < 4 ? N : 4} : (id == 2 || N > 16) ? Layout{16, N / 16} : Layout{64, N / 4};
-}
-inline constexpr int threads_of(int N, int id) { return layout_of(N, id).cb * N / layout_of(N, id).g; }
+inline constexpr Layout layout_of(int N) { return N < 16 ? Layout{64, N < 4 ? N : 4} : Layout{16, N / 16}; }
+inline constexpr int threads_of(int N) { return layout_of(N).cb * N / layout_of(N).g; }
 
 struct Plan {
-  int K, Ku, layout, cb, nblk_d, nchunks, chunk_len;
+  int K, Ku, cb, nblk_d, nchunks, chunk_len;
   size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
   size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
 };
@@ -70,10 +64,10 @@ MSCAN_DECLARE_DISPATCH(f32_simple)
 MSCAN_DECLARE_DISPATCH(f32_exact)
 
 #ifdef MSCAN_INSTANTIATE
-template <typename TIn, int N, int LID, bool EXACT>
+template <typename TIn, int N, bool EXACT>
 int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
-  constexpr Layout lay = layout_of(N, LID);
-  constexpr int NT = threads_of(N, LID);
+  constexpr Layout lay = layout_of(N);
+  constexpr int NT = threads_of(N);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
@@ -88,15 +82,7 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
 
 template <typename TIn, int N, bool EXACT>
 int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
-  int rc = MAMBA_ERR_UNSUPPORTED;
-  if constexpr (N > 16) {
-    rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
-  } else if constexpr (N == 16) {
-    if (pl.layout == 2) rc = launch_chunks<TIn, N, 2, EXACT>(p, pl, stream);
-    else rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
-  } else {
-    rc = launch_chunks<TIn, N, 0, EXACT>(p, pl, stream);
-  }
+  const int rc = launch_chunks<TIn, N, EXACT>(p, pl, stream);
   if (rc != MAMBA_OK) return rc;
   if (p.ws_y && p.out && p.K > 1) {  // (with one direction the scan wrote out itself)
     const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
