@@ -12,12 +12,16 @@ Sources, cited by page title and section:
   [VIM] "Vision Mamba：从状态空间模型到视觉革命的跨越" (x-humanoid.csdn.net)
   [S4M] "从S4到Mamba：选择性状态空间模型的演进与革新" (jsqmd.com)
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against closed
-forms, brute force and invariants the pages fix (LTI convolution [MFS §2.3,
-eq (3a)(3b)], the A = 0 cumulative sum, associativity of the affine scan
-[MFS §5], the first-order limit of the ZOH rule [MUN §4], flip equivariance
-[VIM §2.2], the N = 1 gated-RNN case [MFS §6.2 Step 5, Theorem 1], the
-recurrent/step form [MFS §2.3]).
+Every function here is pinned against something other than itself.
+``tests/test_oracle_pins.py`` pins the scan, the step and the Conv1d against
+closed forms, brute force and invariants the pages fix (LTI convolution [MFS
+§2.3, eq (3a)(3b)], the A = 0 cumulative sum, associativity of the affine
+scan [MFS §5], the first-order limit of the ZOH rule [MUN §4], flip
+equivariance [VIM §2.2], the N = 1 gated-RNN case [MFS §6.2 Step 5, Theorem
+1], the recurrent/step form [MFS §2.3], the Conv1d's impulse response and
+numpy's convolution).  ``tests/test_oracle_bwd_pins.py`` pins the backward
+pass against central finite differences of the forward oracle for every
+gradient, and checks that it is linear in dout.
 """
 from __future__ import annotations
 
