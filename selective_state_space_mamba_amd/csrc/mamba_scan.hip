@@ -61,13 +61,14 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   pl->Ku = (mode == MAMBA_DIR_CROSS2D) ? 1 : K;
   // Layout and time split.  Waves wanted: MSCAN_TARGET_WAVES (3 per SIMD),
   // since one wave alone issues vector instructions at about half the SIMD rate.
-  // Measured on MI355X: at N = 16 the 16-channel blocks beat the 64-channel
-  // ones at every size tried once the wave priorities were in (Vim-224
-  // 239 -> 219 µs, a batch-32 130M-shaped layer 646 -> 491 µs), so N >= 16
-  // always uses them; smaller N has only the 64-channel layout.  Rows short of
-  // waves (long sequences with few rows) are split in time, the 16-channel
-  // layout into enough chunks for ~24 waves per SIMD (32 -> 48 or 64 chunks:
-  // -2 to -3 % on the long workloads).
+  // Measured on MI355X: the 16-channel blocks beat the 64-channel ones at
+  // every size tried once the wave priorities were in (N = 16: Vim-224
+  // 239 -> 219 µs, a batch-32 130M-shaped layer 646 -> 491 µs; that layer at
+  // N = 8: 306 -> 140 µs, at N = 4: 440 -> 148 µs), so every N >= 4 uses
+  // them; N = 1 and 2 have only the 64-channel layout.  Rows short of waves
+  // (long sequences with few rows) are split in time, the 16-channel layout
+  // into enough chunks for ~24 waves per SIMD (32 -> 48 or 64 chunks: -2 to
+  // -3 % on the long workloads).
   const int64_t L = g->seqlen;
   const int cb = layout_of((int)N).cb;
   const int64_t waves = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb) * (threads_of((int)N) / 64);

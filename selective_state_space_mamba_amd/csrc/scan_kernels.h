@@ -129,8 +129,8 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // are in different phases at any time; letting the arbiter prefer one phase
   // shortens the chain of tiles of every wave.  Measured on MI355X: with
   // 16-channel blocks, preferring the scan loop (scan 1, epilogue and staging
-  // 0) took the 130M layer from 151 to 139 µs; with 64-channel blocks (state
-  // sizes below 16), preferring staging over the scan (staging 2, scan 1,
+  // 0) took the 130M layer from 151 to 139 µs; with 64-channel blocks (now
+  // only N = 1 and 2), preferring staging over the scan (staging 2, scan 1,
   // epilogue 0) took Vim-224 from 245 to 238 µs when it still ran on them,
   // where the 16-channel choice gained nothing.
   constexpr int P_SCAN = 1;

@@ -33,15 +33,14 @@ inline constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 #endif
 
 // Workgroup layouts: CB channels per workgroup, G states per thread,
-// CB*N/G threads.  State sizes below 16 use 64-channel blocks with up to 4
-// states per thread (the readout sums N/G partials per (token, channel) and
-// each wave's B, C reads are wave-uniform); state sizes of 16 and above use
-// 16-channel blocks with N/16 states per thread (at most 4), whose waves
-// hold 4 state rows of the same 16 channels.
+// CB*N/G threads.  State sizes from 4 up use 16-channel blocks with one state
+// per thread (N/16 from N = 16 on, at most 4), whose waves hold 4 state rows
+// of the same 16 channels; N = 1 and 2, which cannot fill a wave that way,
+// use 64-channel blocks with all N states in each thread.
 struct Layout {
   int cb, g;
 };
-inline constexpr Layout layout_of(int N) { return N < 16 ? Layout{64, N < 4 ? N : 4} : Layout{16, N / 16}; }
+inline constexpr Layout layout_of(int N) { return N < 4 ? Layout{64, N} : Layout{16, N < 16 ? 1 : N / 16}; }
 inline constexpr int threads_of(int N) { return layout_of(N).cb * N / layout_of(N).g; }
 
 struct Plan {
