@@ -71,7 +71,9 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   // -3 % on the long workloads).
   const int64_t L = g->seqlen;
   const int cb = layout_of((int)N).cb;
-  const int64_t waves = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb) * (threads_of((int)N) / 64);
+  const int64_t rows = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb);
+  const int g16 = (N == 16 && rows * (threads_of(16, 1) / 64) >= kG2Waves) ? 2 : 1;
+  const int64_t waves = rows * (threads_of((int)N, g16) / 64);
   int64_t nch = 1;
   auto split = [&](int64_t target) {
     int64_t c = (target + waves - 1) / waves;
@@ -84,6 +86,7 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
   if (nch < 1) nch = 1;
   pl->cb = cb;
+  pl->g = layout_of((int)N, g16).g;
   pl->nblk_d = (int)((g->dim + cb - 1) / cb);
   int64_t clen = (L + nch - 1) / nch;
   clen = (clen + kTile - 1) / kTile * kTile;

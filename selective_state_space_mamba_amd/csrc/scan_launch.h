@@ -36,15 +36,23 @@ inline constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 // CB*N/G threads.  State sizes from 4 up use 16-channel blocks with one state
 // per thread (N/16 from N = 16 on, at most 4), whose waves hold 4 state rows
 // of the same 16 channels; N = 1 and 2, which cannot fill a wave that way,
-// use 64-channel blocks with all N states in each thread.
+// use 64-channel blocks with all N states in each thread.  At N = 16 a
+// problem with many rows takes 2 states per thread instead (kG2Waves).
 struct Layout {
   int cb, g;
 };
-inline constexpr Layout layout_of(int N) { return N < 4 ? Layout{64, N} : Layout{16, N < 16 ? 1 : N / 16}; }
-inline constexpr int threads_of(int N) { return layout_of(N).cb * N / layout_of(N).g; }
+inline constexpr Layout layout_of(int N, int g16 = 1) {
+  return N < 4 ? Layout{64, N} : N == 16 ? Layout{16, g16} : Layout{16, N < 16 ? 1 : N / 16};
+}
+inline constexpr int threads_of(int N, int g16 = 1) { return layout_of(N, g16).cb * N / layout_of(N, g16).g; }
+// Measured on MI355X (130M-shaped layers, Vim-224): 2 states per thread at
+// N = 16 win once 1 state per thread would give 24 or more waves per SIMD
+// (batch 64: 942 -> 910 µs; Vim-224: 220 -> 210 µs) and lose below 12
+// (batch 32: 482 -> 497; the 130M layer at 3 waves per SIMD: 140 -> 180).
+inline constexpr int64_t kG2Waves = 16 * 1024;
 
 struct Plan {
-  int K, Ku, cb, nblk_d, nchunks, chunk_len;
+  int K, Ku, cb, g, nblk_d, nchunks, chunk_len;
   size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
   size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
 };
@@ -63,10 +71,10 @@ MSCAN_DECLARE_DISPATCH(f32_simple)
 MSCAN_DECLARE_DISPATCH(f32_exact)
 
 #ifdef MSCAN_INSTANTIATE
-template <typename TIn, int N, bool EXACT>
+template <typename TIn, int N, int G16, bool EXACT>
 int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
-  constexpr Layout lay = layout_of(N);
-  constexpr int NT = threads_of(N);
+  constexpr Layout lay = layout_of(N, G16);
+  constexpr int NT = threads_of(N, G16);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
@@ -81,7 +89,12 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
 
 template <typename TIn, int N, bool EXACT>
 int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
-  const int rc = launch_chunks<TIn, N, EXACT>(p, pl, stream);
+  int rc;
+  if constexpr (N == 16) {
+    rc = pl.g == 2 ? launch_chunks<TIn, N, 2, EXACT>(p, pl, stream) : launch_chunks<TIn, N, 1, EXACT>(p, pl, stream);
+  } else {
+    rc = launch_chunks<TIn, N, 1, EXACT>(p, pl, stream);
+  }
   if (rc != MAMBA_OK) return rc;
   if (p.ws_y && p.out && p.K > 1) {  // (with one direction the scan wrote out itself)
     const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;

@@ -77,13 +77,15 @@ SMALL = {
     "split_bwd_bf16": I.Workload("split_bwd_bf16", 1, 64, 3001, 16, I.DIR_BWD, "bf16", True, 22),
     "split_bidir_bf16": I.Workload("split_bidir_bf16", 1, 64, 3000, 16, I.DIR_BIDIR, "bf16", True, 23),
     "split_cross2d_bf16": I.Workload("split_cross2d_bf16", 1, 32, 2304, 16, I.DIR_CROSS2D, "bf16", False, 24, 48, 48),
-    # rows for 768 waves of 64-channel blocks: planned on 16-channel blocks
+    # many rows, short sequences: one state per thread
     "rows768_bf16": I.Workload("rows768_bf16", 12, 1024, 70, 16, I.DIR_FWD, "bf16", True, 25),
     "rows768_cross2d_f32": I.Workload("rows768_cross2d_f32", 3, 1024, 36, 16, I.DIR_CROSS2D, "f32", False, 26, 6, 6),
-    # enough rows for 64-channel blocks of 4 states per thread
     "wide4_bidir_bf16": I.Workload("wide4_bidir_bf16", 16, 1536, 20, 16, I.DIR_BIDIR, "bf16", True, 27),
-    # few rows, long sequence: 16-channel blocks split in time (N = 16), and
-    # 64-channel blocks split in time (N < 16 has only those)
+    # rows for at least 16 waves per SIMD at N = 16: 2 states per thread (with a
+    # ragged channel block and a ragged tile)
+    "g2_fwd_bf16": I.Workload("g2_fwd_bf16", 64, 1032, 45, 16, I.DIR_FWD, "bf16", True, 32),
+    "g2_bidir_f32": I.Workload("g2_bidir_f32", 32, 1032, 37, 16, I.DIR_BIDIR, "f32", True, 33),
+    # few rows, long sequence: split in time (N = 16, 8 and 4)
     "split_long_fwd_bf16": I.Workload("split_long_fwd_bf16", 1, 64, 9000, 16, I.DIR_FWD, "bf16", True, 28),
     "split_long_bidir_f32": I.Workload("split_long_bidir_f32", 1, 64, 8500, 16, I.DIR_BIDIR, "f32", True, 29),
     "split_long_fwd_bf16_n8": I.Workload("split_long_fwd_bf16_n8", 1, 64, 9000, 8, I.DIR_FWD, "bf16", True, 30),
