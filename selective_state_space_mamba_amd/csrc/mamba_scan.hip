@@ -72,7 +72,12 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   const int64_t L = g->seqlen;
   const int cb = layout_of((int)N).cb;
   const int64_t rows = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb);
-  const int g16 = (N == 16 && rows * (threads_of(16, 1) / 64) >= kG2Waves) ? 2 : 1;
+  // 2 states per thread at N = 16 when there are waves to spare, or when the
+  // rows are so few that a time split supplies the waves (97k-token Vim:
+  // 1290 -> 1257 µs; the 262k-token context unchanged)
+  const int64_t waves1 = rows * (threads_of(16, 1) / 64);
+  const bool split_needed = waves1 < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK;
+  const int g16 = (N == 16 && (waves1 >= kG2Waves || split_needed)) ? 2 : 1;
   const int64_t waves = rows * (threads_of((int)N, g16) / 64);
   int64_t nch = 1;
   auto split = [&](int64_t target) {
