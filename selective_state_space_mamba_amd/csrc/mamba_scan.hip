@@ -80,13 +80,18 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   const int g16 = (N == 16 && (waves1 >= kG2Waves || split_needed)) ? 2 : 1;
   const int64_t waves = rows * (threads_of((int)N, g16) / 64);
   int64_t nch = 1;
+  // N = 1, 2 (64-channel blocks, one thread per channel) have so few waves
+  // that they split into chunks as short as 128 positions (the 130M-shaped
+  // layer at N = 1: 370 -> 173 µs in 16 chunks; 64- or 32-position chunks
+  // for 2 or 4 times the waves: 206 and 278 µs)
+  const int64_t min_chunk = cb == 64 ? 128 : MSCAN_MIN_CHUNK;
   auto split = [&](int64_t target) {
     int64_t c = (target + waves - 1) / waves;
-    if (c > L / MSCAN_MIN_CHUNK) c = L / MSCAN_MIN_CHUNK;
+    if (c > L / min_chunk) c = L / min_chunk;
     if (c > MSCAN_MAX_CHUNKS) c = MSCAN_MAX_CHUNKS;
     return c < 1 ? (int64_t)1 : c;
   };
-  if (waves < MSCAN_TARGET_WAVES / 2 && L >= 2 * MSCAN_MIN_CHUNK)
+  if (waves < MSCAN_TARGET_WAVES / 2 && L >= 2 * min_chunk)
     nch = split(cb == 16 ? 8 * MSCAN_TARGET_WAVES : MSCAN_TARGET_WAVES);
   if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
   if (nch < 1) nch = 1;
