@@ -80,11 +80,13 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   const int g16 = (N == 16 && (waves1 >= kG2Waves || split_needed)) ? 2 : 1;
   const int64_t waves = rows * (threads_of((int)N, g16) / 64);
   int64_t nch = 1;
-  // N = 1, 2 (64-channel blocks, one thread per channel) have so few waves
-  // that they split into chunks as short as 128 positions (the 130M-shaped
-  // layer at N = 1: 370 -> 173 µs in 16 chunks; 64- or 32-position chunks
-  // for 2 or 4 times the waves: 206 and 278 µs)
-  const int64_t min_chunk = cb == 64 ? 128 : MSCAN_MIN_CHUNK;
+  // Smaller state sizes have fewer waves per row and split into shorter
+  // chunks: N = 1, 2 (64-channel blocks, one thread per channel) down to 128
+  // positions (the 130M-shaped layer at N = 1: 370 -> 173 µs in 16 chunks;
+  // 64- or 32-position chunks for 2 or 4 times the waves: 206 and 278 µs),
+  // N = 4, 8 down to 256 (N = 4: 149 -> 139 µs); N >= 16 keeps 1024 (shorter
+  // chunks cost the 97k-token Vim image and the long context 1.5-2 %).
+  const int64_t min_chunk = cb == 64 ? 128 : N < 16 ? 256 : MSCAN_MIN_CHUNK;
   auto split = [&](int64_t target) {
     int64_t c = (target + waves - 1) / waves;
     if (c > L / min_chunk) c = L / min_chunk;
