@@ -99,6 +99,10 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   if (nch < 1) nch = 1;
   pl->cb = cb;
   pl->g = layout_of((int)N, g16).g;
+  // the scan loop's raised wave priority pays with few waves per SIMD and
+  // costs with many (the kernel's priority note): below 16 per SIMD (a
+  // batch-32 130M-shaped layer at 12: 478 µs with it, 482 without)
+  pl->prio = waves * nch < 16 * 1024 ? 1 : 0;
   pl->nblk_d = (int)((g->dim + cb - 1) / cb);
   int64_t clen = (L + nch - 1) / nch;
   clen = (clen + kTile - 1) / kTile * kTile;

@@ -77,6 +77,7 @@ struct ScanParams {
   int nblk_d;               // channel blocks of 64
   int softplus;
   int ckpt_tiles;           // tiles of TT positions per sequence (checkpoint rows)
+  int prio;                 // 1: the scan loop runs at raised wave priority (16-channel blocks)
 };
 // Template flag EXACT of the kernels below: exact zero-order-hold input term
 // ((e^{ΔA} - 1)/A)·B·u instead of Δ·B·u [MFS §6.2 Step 4, eq (4)].
@@ -128,12 +129,14 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // Wave priorities (s_setprio) of a tile's phases.  The few waves per SIMD
   // are in different phases at any time; letting the arbiter prefer one phase
   // shortens the chain of tiles of every wave.  Measured on MI355X: with
-  // 16-channel blocks, preferring the scan loop (scan 1, epilogue and staging
-  // 0) took the 130M layer from 151 to 139 µs; with 64-channel blocks (now
-  // only N = 1 and 2), preferring staging over the scan (staging 2, scan 1,
-  // epilogue 0) took Vim-224 from 245 to 238 µs when it still ran on them,
-  // where the 16-channel choice gained nothing.
-  constexpr int P_SCAN = 1;
+  // 16-channel blocks and few waves per SIMD (p.prio, set by the plan),
+  // preferring the scan loop (scan 1, epilogue and staging 0) took the 130M
+  // layer from 151 to 139 µs (3 waves per SIMD) and the 130M-shaped layer at
+  // N = 32 / 64 from 220 / 401 to 204 / 367 µs; with many waves no preference
+  // is better (Vim-224 at 24 waves per SIMD 211 -> 206 µs, the 262k-token
+  // context 4.22 -> 4.02 ms); with 64-channel blocks (now only N = 1 and 2),
+  // preferring staging over the scan (staging 2, scan 1, epilogue 0) took
+  // Vim-224 from 245 to 238 µs when it still ran on them.
   constexpr int P_EPI = 0;
   constexpr int P_STAGE = CB == 16 ? 0 : 2;
   __shared__ float s_y[AGG ? 1 : NY][AGG ? 1 : CB][AGG ? 4 : YS];
@@ -398,7 +401,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
       }
     };
-    __builtin_amdgcn_s_setprio(P_SCAN);
+    if (CB == 64 || p.prio) __builtin_amdgcn_s_setprio(1);
     Ops o0, o1;
     read_ops(o0, 0);
 #pragma unroll

@@ -52,7 +52,7 @@ inline constexpr int threads_of(int N, int g16 = 1) { return layout_of(N, g16).c
 inline constexpr int64_t kG2Waves = 16 * 1024;
 
 struct Plan {
-  int K, Ku, cb, g, nblk_d, nchunks, chunk_len;
+  int K, Ku, cb, g, nblk_d, nchunks, chunk_len, prio;
   size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
   size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
 };
@@ -77,12 +77,14 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
   constexpr int NT = threads_of(N, G16);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
+    p.prio = pl.prio;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
     hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.grid_chunks = pl.nchunks;
   const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
+  p.prio = pl.prio;
   hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
 }
