@@ -207,7 +207,7 @@ def test_saved_state_small(case):
     saved_vs_recompute(name, w, dev_inputs(x), to_dev(dout), to_dev(init), softplus, exact)
 
 
-@pytest.mark.parametrize("wname", ["mamba130m_layer", "vmamba_ss2d"])
+@pytest.mark.parametrize("wname", ["mamba130m_layer", "vmamba_ss2d", "vim_bidir_224"])
 def test_saved_state_full_size(wname):
     w = I.WORKLOADS[wname]
     announce("saved full %s" % (w,))
