@@ -166,6 +166,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=512)
     ap.add_argument("--conv-steps", type=int, default=20, help="timed calls of the Conv1d + SiLU prologue (0: skip)")
     ap.add_argument("--bwd-steps", type=int, default=10, help="timed calls of the backward pass (0: skip)")
+    ap.add_argument("--variant-steps", type=int, default=20,
+                    help="timed calls of each forward option (exact ZOH, initial state; 0: skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, run one torch elementwise kernel that reads and writes a "
                          "MIB-MiB buffer (known bytes, used to scale rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -306,6 +308,45 @@ def main():
                 "us_per_call": conv_s * 1e6, "algorithmic_bytes": cbytes, "achieved_gbs": cbytes / conv_s / 1e9,
                 "peak_gbs": HBM_PEAK_GBS, "frac": cbytes / conv_s / 1e9 / HBM_PEAK_GBS, "bound": "hbm"}
 
+    variants = None
+    if args.variant_steps > 0:
+        # the forward options on the same inputs, timed like the plain forward
+        # (HIP events on the launch stream around each call)
+        inits = [torch.randn(st.shape, dtype=torch.float32, device=dev, generator=torch.Generator(dev).manual_seed(7 + j))
+                 for j, st in enumerate(states)]
+
+        def vstep(i, **kw):
+            s = sets[i % len(sets)]
+            ms.scan_fwd(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"],
+                        dir_mode=w.dir_mode, height=w.height, width=w.width, out=outs[i % len(sets)],
+                        last_state=states[i % len(sets)], workspace=ws, stream=stream, **kw)
+
+        # the three calls interleaved, so that each sees the same clocks
+        fns = [vstep, lambda i: vstep(i, exact_zoh=True), lambda i: vstep(i, initial_state=inits[i % len(inits)])]
+        with torch.cuda.stream(stream):
+            for i in range(20):
+                for fn in fns:
+                    fn(i)
+            torch.cuda.synchronize()
+            evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+                   for _ in range(args.variant_steps)]
+            for i in range(args.variant_steps):
+                for j, fn in enumerate(fns):
+                    evs[i][j][0].record(stream)
+                    fn(i)
+                    evs[i][j][1].record(stream)
+            torch.cuda.synchronize()
+        plain_s, exact_s, init_s = (float(np.mean([e[j][0].elapsed_time(e[j][1]) for e in evs])) * 1e-3
+                                    for j in range(len(fns)))
+        variants = {"plain_us_per_call": plain_s * 1e6,
+                    "exact_zoh": {"op": "forward with the exact zero-order hold for the input term",
+                                  "us_per_call": exact_s * 1e6, "elements_per_s": el / exact_s,
+                                  "vs_plain": exact_s / plain_s},
+                    "initial_state": {"op": "forward resumed from a given [B][K][D][N] float32 state",
+                                      "us_per_call": init_s * 1e6, "elements_per_s": el / init_s,
+                                      "vs_plain": init_s / plain_s}}
+        del inits
+
     bwd = None
     if args.bwd_steps > 0 and w.dstate <= 16:
         douts = [todev(I.make_dout(w.with_(seed=w.seed + 1000 * s_))) for s_ in range(len(sets))]
@@ -415,6 +456,7 @@ def main():
         "decode": decode,
         "conv1d": conv,
         "backward": bwd,
+        "variants": variants,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)
