@@ -83,6 +83,34 @@ def assert_close(name, got, want, dtype):
     assert emax <= tol["max"] and el2 <= tol["l2"], (name, emax, el2)
 
 
+def saturate(w: I.Workload, x: dict, seed: int) -> dict:
+    """Copy of inputs x with Δraw and z pushed far outside their usual range:
+    a fifth of Δraw in [-30, -15] (softplus underflows, Δ ~ 0: the state
+    carries over unchanged), a tenth in [52, 70] (softplus(Δraw + bias) = Δraw +
+    bias, past the clamp of its exponential: the decay vanishes), and a fifth
+    of z at ±[20, 100] (the gate's exponential overflows or vanishes)."""
+    r = np.random.Generator(np.random.PCG64([seed, 9]))
+    y = dict(x)
+
+    def widen(v):
+        return I.bf16_to_f32(v) if w.dtype == "bf16" else np.asarray(v, np.float32)
+
+    def narrow(v):
+        return I.bf16_bits(v) if w.dtype == "bf16" else v.astype(np.float32)
+
+    dl = widen(x["delta"]).copy()
+    pick = r.uniform(size=dl.shape)
+    dl = np.where(pick < 0.2, r.uniform(-30.0, -15.0, dl.shape), dl)
+    dl = np.where(pick > 0.9, r.uniform(52.0, 70.0, dl.shape), dl)
+    y["delta"] = narrow(dl.astype(np.float32))
+    if x.get("z") is not None:
+        zz = widen(x["z"]).copy()
+        pick = r.uniform(size=zz.shape)
+        mag = r.uniform(20.0, 100.0, zz.shape) * np.where(r.uniform(size=zz.shape) < 0.5, -1.0, 1.0)
+        y["z"] = narrow(np.where(pick < 0.2, mag, zz).astype(np.float32))
+    return y
+
+
 def sample_rows(rng, batch, dim, n):
     """n distinct (b, d) rows, always including the first and last channel."""
     rows = {(0, 0), (batch - 1, dim - 1)}

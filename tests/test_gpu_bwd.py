@@ -20,7 +20,7 @@ import oracle
 import selective_state_space_mamba_amd as ms
 from selective_state_space_mamba_amd import inputs as I
 
-from scanutil import assert_close, dev_inputs, from_dev, to_dev, torch
+from scanutil import assert_close, dev_inputs, from_dev, saturate, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -144,6 +144,19 @@ def test_bwd_exact_mixed_A():
     got = gpu_bwd(w, x, dout, exact=True)
     ref = oracle_bwd(w, x, dout, exact=True)
     compare("exact_mixedA", w, got, ref)
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[3], SMALL[6]], ids=["fwd_bf16", "bidir_f32", "cross2d_f32_n1"])
+def test_bwd_saturated_softplus_and_gate(case):
+    """Every gradient with Δraw and z far outside their usual range (softplus
+    underflowing and past its clamp, the gate's exponential overflowing)."""
+    name, w, softplus, exact, with_init, skip = case
+    announce("bwd saturated %s %s" % (name, w))
+    x, dout, init = small_inputs(case)
+    x = saturate(w, x, w.seed)
+    got = gpu_bwd(w, x, dout, softplus=softplus, exact=exact, init=init)
+    ref = oracle_bwd(w, x, dout, softplus=softplus, exact=exact, init=init)
+    compare("saturated_" + name, w, got, ref)
 
 
 def test_bwd_optional_outputs_absent():

@@ -16,8 +16,8 @@ import oracle
 import selective_state_space_mamba_amd as ms
 from selective_state_space_mamba_amd import inputs as I
 
-from scanutil import (TOL, assert_close, dev_inputs, errors, from_dev, gpu_fwd, oracle_fwd, sample_rows, to_dev,
-                      torch)
+from scanutil import (TOL, assert_close, dev_inputs, errors, from_dev, gpu_fwd, oracle_fwd, sample_rows, saturate,
+                      to_dev, torch)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -130,6 +130,29 @@ def test_initial_state():
     w = I.Workload("init_split", 1, 64, 3000, 16, I.DIR_FWD, "bf16", True, 33)
     init = np.random.Generator(np.random.PCG64(6)).standard_normal((1, 64, 16)).astype(np.float32)
     run_and_check(w, I.make_inputs(w), name="init_state_split", initial_state=to_dev(init))
+
+
+SATURATED = [
+    (I.Workload("saturated_fwd", 2, 48, 150, 16, I.DIR_FWD, "bf16", True, 52), False),
+    (I.Workload("saturated_bidir", 1, 32, 97, 16, I.DIR_BIDIR, "f32", True, 53), True),
+    (I.Workload("saturated_cross", 1, 16, 48, 8, I.DIR_CROSS2D, "bf16", True, 54, 6, 8), False),
+]
+
+
+@pytest.mark.parametrize("w,exact", SATURATED, ids=[c[0].name for c in SATURATED])
+def test_saturated_softplus_and_gate(w, exact):
+    """Δraw and z far outside their usual range [MFS §4.1 (softplus), §6.2 Step 6
+    (silu gate)]: finite results equal to the oracle's, also row by row
+    ((b, d) over the sequence, each against its own largest value), so that
+    the rows with large Δ do not hide the others."""
+    x = saturate(w, I.make_inputs(w), w.seed)
+    out, _, ref_out, _ = run_and_check(w, x, name=w.name + ("_exact" if exact else ""), exact_zoh=exact)
+    got = from_dev(out)
+    ref = ref_out.reshape(got.shape)
+    scale = np.max(np.abs(ref), axis=1)
+    err = np.max(np.abs(got - ref), axis=1) / np.where(scale > 0, scale, 1.0)
+    print("%s: row-wise max err %.3e" % (w.name, err.max()), flush=True)
+    assert err.max() <= TOL[w.dtype]["max"], err.max()
 
 
 def test_no_last_state():
