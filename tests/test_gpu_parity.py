@@ -270,8 +270,10 @@ def test_cross_scan_transpose_symmetry():
 # ---------------------------------------------------------------------------------------------
 # decode step
 
-def run_decode(w, L0, steps, rows=None, exact_zoh=False):
+def run_decode(w, L0, steps, rows=None, exact_zoh=False, saturated=False):
     x = I.make_inputs(w, seqlen=L0 + steps)
+    if saturated:
+        x = saturate(w, x, w.seed)
     head = {k: (v[:, :L0] if k in ("u", "delta", "B", "C", "z") else v) for k, v in x.items()}
     xd = dev_inputs({k: (np.ascontiguousarray(v) if v is not None else None) for k, v in head.items()})
     announce("decode %s L0=%d steps=%d" % (w.name, L0, steps))
@@ -300,6 +302,16 @@ def test_decode_continues_scan_small():
     got, st, ref_out, ref_st = run_decode(wf, 64, 16)
     assert_close("decode f32 out", got, ref_out[:, 64:], "f32")
     assert_close("decode f32 state", st, ref_st[:, 0], "f32")
+
+
+def test_decode_saturated_softplus_and_gate():
+    """Decode steps (and the scan before them) with Δraw and z far outside
+    their usual range, as in the saturated forward cases."""
+    for w, exact in ((I.Workload("dec_sat", 2, 72, 0, 16, I.DIR_FWD, "bf16", True, 55), False),
+                     (I.Workload("dec_sat_f32", 1, 40, 0, 8, I.DIR_FWD, "f32", True, 56), True)):
+        got, st, ref_out, ref_st = run_decode(w, 70, 24, exact_zoh=exact, saturated=True)
+        assert_close(w.name + " out", got, ref_out[:, 70:], w.dtype)
+        assert_close(w.name + " state", st, ref_st[:, 0], w.dtype)
 
 
 @pytest.mark.parametrize("N", [1, 2, 8, 32, 64])
