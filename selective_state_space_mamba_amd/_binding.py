@@ -112,6 +112,21 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _foreign_stream(stream):
+    """The launch stream as a torch stream when it is not torch's current
+    stream, else None.  A wrapper that will allocate (outputs, workspace,
+    saved state) then calls itself again with that stream current, so that
+    its tensors come from the caching allocator's pool of the stream the
+    library launches on and a workspace dropped on return is not handed to
+    another stream while the launch may still be using it.  A call given all
+    its buffers skips the check (it costs a few microseconds of host time)."""
+    import torch
+    if stream is None:
+        return None
+    ts = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+    return None if ts.cuda_stream == torch.cuda.current_stream(ts.device).cuda_stream else ts
+
+
 def make_dims(batch, dim, seqlen, dstate, dtype, *, height=0, width=0, delta_softplus=True, exact_zoh=False,
               initial_state=None, workspace=None, workspace_bytes=0) -> MambaDims:
     return MambaDims(int(batch), int(dim), int(seqlen), int(dstate), int(height), int(width), int(dtype),
@@ -182,6 +197,13 @@ def scan_fwd_save(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mod
 def _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus, exact_zoh, initial_state,
          out, last_state, want_last_state, workspace, stream, save, saved):
     import torch
+    allocates = (out is None or workspace is None or (last_state is None and want_last_state)
+                 or (save and saved is None))
+    ts = _foreign_stream(stream) if allocates else None
+    if ts is not None:
+        with torch.cuda.stream(ts):
+            return _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus, exact_zoh,
+                        initial_state, out, last_state, want_last_state, workspace, ts, save, saved)
     lib = load_library()
     K = num_dirs(dir_mode)
     dev = u.device
@@ -241,6 +263,13 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dout, dir_mo
     None unless want_dinit).  saved: the buffer scan_fwd_save returned for
     the same arguments (the forward recompute is then skipped), or None."""
     import torch
+    ts = _foreign_stream(stream)
+    if ts is not None:
+        with torch.cuda.stream(ts):
+            return scan_bwd(u, delta, A, B, C, D, z, delta_bias, dout=dout, dir_mode=dir_mode, height=height,
+                            width=width, delta_softplus=delta_softplus, exact_zoh=exact_zoh,
+                            initial_state=initial_state, want_dinit=want_dinit, workspace=workspace, saved=saved,
+                            stream=ts)
     lib = load_library()
     K = num_dirs(dir_mode)
     dev = u.device
@@ -288,6 +317,11 @@ def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=Non
     place), u_t/delta_t/z_t [B][D], B_t/C_t [B][N], A [D][N], D/delta_bias [D].
     Returns out [B][D]."""
     import torch
+    ts = _foreign_stream(stream) if out is None else None
+    if ts is not None:
+        with torch.cuda.stream(ts):
+            return scan_step(state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, delta_softplus=delta_softplus,
+                             exact_zoh=exact_zoh, out=out, stream=ts)
     lib = load_library()
     dev = u_t.device
     dt = _dtype_code(u_t)
@@ -316,6 +350,10 @@ def conv1d_silu(x, weight, bias=None, *, reverse=False, out=None, stream=None):
     """mamba_conv1d_silu on torch tensors: x [B][L][D] (bfloat16 or float32),
     weight [D][W] float32, bias [D] float32 or None.  Returns out [B][L][D]."""
     import torch
+    ts = _foreign_stream(stream) if out is None else None
+    if ts is not None:
+        with torch.cuda.stream(ts):
+            return conv1d_silu(x, weight, bias, reverse=reverse, out=out, stream=ts)
     lib = load_library()
     dev = x.device
     Bsz, L, Dm = x.shape

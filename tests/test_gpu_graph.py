@@ -153,3 +153,46 @@ def test_two_streams():
     for k in seq[4]:
         if seq[4][k] is not None:
             assert t.equal(seq[4][k], par[4][k]), k
+
+
+def test_side_stream_allocations_belong_to_the_launch_stream():
+    """Calls on a stream other than torch's current one (a torch stream, then a
+    raw handle), with no workspace given, allocate their workspace and outputs
+    from the launch stream's pool.  Right after each call the current stream
+    fills fresh allocations of the workspace's size; had the dropped workspace
+    gone back to the current stream's pool, those fills could overwrite it
+    while the scan still ran.  Every result equals the plain call's."""
+    t = torch()
+    w = W("side_split", 1, 64, 4133, 16, I.DIR_FWD, "bf16", True, 67)  # time split: needs a workspace
+    announce("side stream %s" % (w,))
+    xd = dev_inputs(I.make_inputs(w))
+    dout = dev_inputs({"g": I.make_dout(w)})["g"]
+    dims = ms.make_dims(w.batch, w.dim, w.seqlen, w.dstate, ms.DTYPE_BF16)
+    ws_need = ms.workspace_bytes(dims, w.dir_mode)
+    bws_need = ms.bwd_workspace_bytes(dims, w.dir_mode)
+    assert ws_need > 0
+
+    def fwd(stream=None):
+        return ms.scan_fwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd["D"], xd["z"], xd["delta_bias"],
+                           stream=stream)
+
+    def bwd(stream=None):
+        return ms.scan_bwd(xd["u"], xd["delta"], xd["A"], xd["B"], xd["C"], xd["D"], xd["z"], xd["delta_bias"],
+                           dout=dout, stream=stream)
+
+    ref_out, ref_st = fwd()
+    ref_g = bwd()
+    t.cuda.synchronize()
+    s = t.cuda.Stream()
+    s.wait_stream(t.cuda.current_stream())
+    got, junk = [], []
+    for rep in range(4):
+        handle = s if rep % 2 == 0 else s.cuda_stream
+        got.append((fwd(handle), bwd(handle)))
+        junk += [t.empty(n, dtype=t.uint8, device="cuda:0").fill_(255) for n in (ws_need, bws_need)]
+    t.cuda.synchronize()
+    for rep, ((o, st), g) in enumerate(got):
+        assert t.equal(o, ref_out) and t.equal(st, ref_st), "call %d" % rep
+        for k, v in ref_g.items():
+            if v is not None:
+                assert t.equal(g[k], v), "call %d %s" % (rep, k)
