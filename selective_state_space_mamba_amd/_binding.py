@@ -168,6 +168,17 @@ def _check(t, name, shape, dtype, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _check_buffer(t, name, device):
+    """A caller's workspace or saved-state buffer: any dtype, passed on as its
+    bytes, so it must be one contiguous block on the device of the inputs."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0, width=0,
              delta_softplus=True, exact_zoh=False, initial_state=None, out=None, last_state=None,
              want_last_state=True, workspace=None, stream=None):
@@ -230,6 +241,8 @@ def _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_sof
     _check(last_state, "last_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
     dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
                      exact_zoh=exact_zoh, initial_state=initial_state)
+    _check_buffer(workspace, "workspace", dev)
+    _check_buffer(saved, "saved", dev)
     need = workspace_bytes(dims, dir_mode)
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -296,6 +309,8 @@ def scan_bwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dout, dir_mo
              dinit=torch.empty((Bsz,) + kx + (Dm, N), dtype=torch.float32, device=dev) if want_dinit else None)
     dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
                      exact_zoh=exact_zoh, initial_state=initial_state)
+    _check_buffer(workspace, "workspace", dev)
+    _check_buffer(saved, "saved", dev)
     need = bwd_workspace_bytes(dims, dir_mode)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

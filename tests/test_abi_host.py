@@ -207,3 +207,22 @@ def test_saved_state_size_and_fwd_save_validation(lib):
     assert fwd_save(d, saved_bytes=ck - 1) == E.MAMBA_ERR_WORKSPACE
     assert fwd_save(d, z=FAKE) == E.MAMBA_ERR_WORKSPACE  # with a gate the rows are saved too
     assert fwd_save(d, mode=ms.DIR_BIDIR, saved_bytes=10 ** 9) == E.MAMBA_ERR_WORKSPACE  # the forward's own
+
+
+def test_binding_rejects_scattered_buffers(lib):
+    """The torch binding passes a caller's workspace and saved-state buffers on
+    as plain byte ranges, so it refuses a non-contiguous view before any call
+    into the library (CPU tensors: the check comes first)."""
+    import torch
+    Bz, L, Dm, N = 1, 64, 8, 4
+    u = torch.zeros(Bz, L, Dm)
+    A = -torch.ones(Dm, N)
+    Bm = torch.zeros(Bz, L, N)
+    scattered = torch.zeros(64, 8, dtype=torch.uint8).t()
+    assert not scattered.is_contiguous()
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        ms.scan_fwd(u, u, A, Bm, Bm, workspace=scattered)
+    with pytest.raises(ValueError, match="saved must be contiguous"):
+        ms.scan_fwd_save(u, u, A, Bm, Bm, saved=scattered)
+    with pytest.raises(ValueError, match="workspace must be contiguous"):
+        ms.scan_bwd(u, u, A, Bm, Bm, dout=u, workspace=scattered)
