@@ -388,12 +388,12 @@ def test_exact_zoh_is_the_gated_rnn():
 # ---------------------------------------------------------------------------------------------
 # the specified workloads at full size, sampled rows
 
-def full_size_check(w, nrows=48, seed=7):
+def full_size_check(w, nrows=48, seed=7, exact_zoh=False):
     x = I.make_inputs(w)
-    announce("full-size %s" % w.name)
-    out, st = gpu_fwd(w, dev_inputs(x))
+    announce("full-size %s exact_zoh=%s" % (w.name, exact_zoh))
+    out, st = gpu_fwd(w, dev_inputs(x), exact_zoh=exact_zoh)
     rows = sample_rows(np.random.Generator(np.random.PCG64(seed)), w.batch, w.dim, nrows)
-    ref_out, ref_st = oracle_fwd(w, x, rows=rows)
+    ref_out, ref_st = oracle_fwd(w, x, rows=rows, exact_zoh=exact_zoh)
     o = from_dev(out)
     s = from_dev(st).reshape(w.batch, w.ndirs, w.dim, w.dstate)
     got_o = np.stack([o[b, :, d] for b, d in rows])
@@ -407,6 +407,13 @@ def full_size_check(w, nrows=48, seed=7):
                                   "vmamba_ss2d"])
 def test_full_size_workloads(name):
     full_size_check(I.WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", ["mamba130m_layer", "vim_bidir_224"])
+def test_full_size_exact_zoh(name):
+    """The exact input-term rule in the launch configuration the benchmark
+    times for it, sampled rows against the oracle."""
+    full_size_check(I.WORKLOADS[name], exact_zoh=True)
 
 
 @pytest.mark.slow
