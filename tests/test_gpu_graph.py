@@ -1,4 +1,5 @@
-"""The scan entry points inside captured HIP graphs and on concurrent streams.
+"""The scan entry points (forward, backward, decode step) inside captured HIP
+graphs and on concurrent streams.
 
 A launch-bound loop (the one-token decode step, or many short scans) can be
 captured once as a HIP graph and replayed with no host work per call.  The
@@ -196,3 +197,45 @@ def test_side_stream_allocations_belong_to_the_launch_stream():
         for k, v in ref_g.items():
             if v is not None:
                 assert t.equal(g[k], v), "call %d %s" % (rep, k)
+
+
+GRAPH_BWD = [
+    W("graph_bwd_split", 1, 64, 4133, 16, I.DIR_FWD, "bf16", True, 68),  # time-split recompute and adjoint
+    W("graph_bwd_bidir", 2, 32, 300, 16, I.DIR_BIDIR, "bf16", True, 69),
+    W("graph_bwd_cross", 1, 32, 96, 8, I.DIR_CROSS2D, "f32", True, 70, 8, 12),
+]
+
+
+@pytest.mark.parametrize("w", GRAPH_BWD, ids=[w.name for w in GRAPH_BWD])
+def test_bwd_graph_replays(w):
+    """The backward pass (forward recompute, adjoint sweep, sums) captured once
+    and replayed, with other eager backward calls between the replays."""
+    t = torch()
+    announce("graph bwd %s" % (w,))
+    xd = dev_inputs(I.make_inputs(w))
+    other = dev_inputs(I.make_inputs(w.with_(seed=w.seed + 100)))
+    dout = dev_inputs({"g": I.make_dout(w)})["g"]
+
+    def bwd(x, stream=None):
+        return ms.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], x.get("D"), x.get("z"), x.get("delta_bias"),
+                           dout=dout, dir_mode=w.dir_mode, height=w.height, width=w.width, stream=stream)
+
+    ref = bwd(xd)
+    t.cuda.synchronize()
+    graph = t.cuda.CUDAGraph()
+    cs = t.cuda.Stream()
+    cs.wait_stream(t.cuda.current_stream())
+    with t.cuda.graph(graph, stream=cs):
+        got = bwd(xd, cs)
+    t.cuda.synchronize()
+    for rep in range(3):
+        for v in got.values():
+            if v is not None:
+                v.fill_(0)
+        bwd(other)  # eager work between replays
+        t.cuda.synchronize()
+        graph.replay()
+        t.cuda.synchronize()
+        for k, v in ref.items():
+            if v is not None:
+                assert t.equal(got[k], v), "%s replay %d %s" % (w.name, rep, k)
