@@ -226,3 +226,16 @@ def test_binding_rejects_scattered_buffers(lib):
         ms.scan_fwd_save(u, u, A, Bm, Bm, saved=scattered)
     with pytest.raises(ValueError, match="workspace must be contiguous"):
         ms.scan_bwd(u, u, A, Bm, Bm, dout=u, workspace=scattered)
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch) exits
+    with a message before touching a GPU."""
+    import subprocess
+    import sys
+    for args, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + args, capture_output=True, text=True,
+                           env=dict(os.environ, **env), timeout=120)
+        assert r.returncode == 2, (args, env, r.returncode)
+        assert "measures one GPU" in r.stderr
+        assert r.stdout == ""
