@@ -26,8 +26,10 @@
  *     position in the original (grid) order, never by scan order.
  *   - All pointers are device pointers (HIP device memory) unless stated
  *     otherwise.  The caller owns every buffer.  The library allocates no
- *     memory, keeps no state between calls and is safe to call from several
- *     host threads.  Calls on the same buffers must not overlap.
+ *     memory and is safe to call from several host threads.  Calls on the
+ *     same buffers must not overlap.  Its only state is the static device
+ *     scratch of mamba_scan_fwd_noalloc (and that scratch's address on each
+ *     device, looked up once).
  *   - Calls are asynchronous on `stream` (0 = the null stream).  The return
  *     value reports host-side validation and launch errors only; faults during
  *     execution surface at the next synchronisation of the stream.
@@ -59,8 +61,13 @@ typedef enum {
                                  several directions (and for mamba_scan_bwd) seqlen*dim*4
                                  at most 2^31 bytes; seqlen and dim*4 below 2^24 */
   MAMBA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than mamba_scan_fwd_workspace_bytes() */
-  MAMBA_ERR_HIP = -4          /* the HIP runtime rejected a launch */
+  MAMBA_ERR_HIP = -4,         /* the HIP runtime rejected a launch */
+  MAMBA_ERR_SCRATCH = -5      /* mamba_scan_fwd_noalloc: the problem needs more scratch than the
+                                 library's static array holds (MAMBA_NOALLOC_SCRATCH_BYTES) */
 } mamba_status;
+
+/* Size of the static device scratch that mamba_scan_fwd_noalloc uses. */
+#define MAMBA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Scan directions.  K is the number of directions each mode runs.
  *   MAMBA_DIR_FWD      K=1: tokens 0..L-1.
@@ -133,6 +140,28 @@ MAMBA_API size_t mamba_scan_fwd_workspace_bytes(const mamba_dims* dims, int dir_
 MAMBA_API int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
                    int dir_mode, void* out, float* last_state, hipStream_t stream);
+
+/*
+ * mamba_scan_fwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, layouts, results and errors as mamba_scan_fwd, except that
+ * dims->workspace and dims->workspace_bytes are ignored: the scratch the scan
+ * needs (mamba_scan_fwd_workspace_bytes(dims, dir_mode) bytes) comes from a
+ * static device array of MAMBA_NOALLOC_SCRATCH_BYTES (32 MiB) inside the
+ * library, one per device, which each device holds until the process ends.
+ * The call allocates and frees nothing.  A problem that needs more scratch
+ * returns MAMBA_ERR_SCRATCH before any GPU work.  The scratch is looked up
+ * (hipGetSymbolAddress) on the first call on each device, the device of
+ * `stream` (the current device for the null stream); MAMBA_ERR_HIP if that
+ * fails.  Nothing in the scratch has to start at zero: every call writes
+ * what it reads.  Calls that overlap in time on one device (concurrent
+ * streams, several host threads) share that device's array and race; the
+ * caller serialises them.  The caller still passes every input and output.
+ */
+MAMBA_API int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                                     const void* C, const float* D, const void* z, const float* delta_bias,
+                                     const mamba_dims* dims, int dir_mode, void* out, float* last_state,
+                                     hipStream_t stream);
 
 /*
  * One recurrent step of a forward scan (decode) [MFS §2.3: the recurrent form

@@ -13,11 +13,14 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmamba_scan.so")
 
-MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP = 0, -1, -2, -3, -4
+MAMBA_OK, MAMBA_ERR_INVALID, MAMBA_ERR_UNSUPPORTED, MAMBA_ERR_WORKSPACE, MAMBA_ERR_HIP, MAMBA_ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 DIR_FWD, DIR_BWD, DIR_BIDIR, DIR_CROSS2D = 0, 1, 2, 3
 DTYPE_F32, DTYPE_BF16 = 0, 1
 EXPORTED = ("mamba_conv1d_silu", "mamba_scan_bwd", "mamba_scan_bwd_workspace_bytes", "mamba_scan_fwd_workspace_bytes",
-            "mamba_scan_fwd", "mamba_scan_fwd_save", "mamba_scan_saved_bytes", "mamba_scan_step",
+            "mamba_scan_fwd", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_save", "mamba_scan_saved_bytes",
+            "mamba_scan_step",
             "mamba_status_string")
 
 
@@ -60,6 +63,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mamba_scan_fwd_workspace_bytes.argtypes = [ctypes.POINTER(MambaDims), i32]
     lib.mamba_scan_fwd.restype = i32
     lib.mamba_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), i32, vp, vp, vp]
+    lib.mamba_scan_fwd_noalloc.restype = i32
+    lib.mamba_scan_fwd_noalloc.argtypes = lib.mamba_scan_fwd.argtypes
     lib.mamba_scan_step.restype = i32
     lib.mamba_scan_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(MambaDims), vp, vp]
     lib.mamba_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -179,6 +184,26 @@ def _check_buffer(t, name, device):
         raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
+def _torch_f32():
+    import torch
+    return torch.float32
+
+
+def _check_fwd_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, dir_mode, K, Bsz, L, Dm, N, tdt, dev):
+    f32 = _torch_f32()
+    kx = () if K == 1 else (K,)
+    ux = () if (K == 1 or dir_mode == DIR_CROSS2D) else (K,)
+    _check(u, "u", (Bsz,) + ux + (L, Dm), tdt, dev)
+    _check(delta, "delta", (Bsz,) + kx + (L, Dm), tdt, dev)
+    _check(B, "B", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(C, "C", (Bsz,) + kx + (L, N), tdt, dev)
+    _check(z, "z", (Bsz, L, Dm), tdt, dev)
+    _check(A, "A", kx + (Dm, N), f32, dev)
+    _check(D, "D", kx + (Dm,), f32, dev)
+    _check(delta_bias, "delta_bias", kx + (Dm,), f32, dev)
+    _check(initial_state, "initial_state", (Bsz,) + kx + (Dm, N), f32, dev)
+
+
 def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0, width=0,
              delta_softplus=True, exact_zoh=False, initial_state=None, out=None, last_state=None,
              want_last_state=True, workspace=None, stream=None):
@@ -191,6 +216,33 @@ def scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR
     out, last_state, _ = _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_softplus,
                               exact_zoh, initial_state, out, last_state, want_last_state, workspace, stream,
                               False, None)
+    return out, last_state
+
+
+def scan_fwd_noalloc(u, delta, A, B, C, D=None, z=None, delta_bias=None, *, dir_mode=DIR_FWD, height=0,
+                     width=0, delta_softplus=True, exact_zoh=False, initial_state=None, out, last_state=None,
+                     stream=None):
+    """mamba_scan_fwd_noalloc on torch tensors: the forward pass with its scratch
+    taken from the library's static device array (no workspace argument).  The
+    caller passes out [B][L][D] and, if wanted, last_state [B][K][D][N]; this
+    wrapper allocates nothing.  Returns (out, last_state)."""
+    lib = load_library()
+    K = num_dirs(dir_mode)
+    dev = u.device
+    dt = _dtype_code(u)
+    tdt = u.dtype
+    Bsz, L, Dm = delta.shape[0], delta.shape[-2], delta.shape[-1]
+    N = B.shape[-1]
+    _check_fwd_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, dir_mode, K, Bsz, L, Dm, N, tdt, dev)
+    _check(out, "out", (Bsz, L, Dm), tdt, dev)
+    _check(last_state, "last_state", (Bsz,) + (() if K == 1 else (K,)) + (Dm, N), _torch_f32(), dev)
+    dims = make_dims(Bsz, Dm, L, N, dt, height=height, width=width, delta_softplus=delta_softplus,
+                     exact_zoh=exact_zoh, initial_state=initial_state)
+    rc = lib.mamba_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(delta_bias), ctypes.byref(dims), int(dir_mode), _ptr(out),
+                                    _ptr(last_state), _stream(stream))
+    if rc != MAMBA_OK:
+        raise MambaError(rc, "mamba_scan_fwd_noalloc")
     return out, last_state
 
 
@@ -223,16 +275,7 @@ def _fwd(u, delta, A, B, C, D, z, delta_bias, dir_mode, height, width, delta_sof
     Bsz, L, Dm = delta.shape[0], delta.shape[-2], delta.shape[-1]
     N = B.shape[-1]
     kx = () if K == 1 else (K,)
-    ux = () if (K == 1 or dir_mode == DIR_CROSS2D) else (K,)
-    _check(u, "u", (Bsz,) + ux + (L, Dm), tdt, dev)
-    _check(delta, "delta", (Bsz,) + kx + (L, Dm), tdt, dev)
-    _check(B, "B", (Bsz,) + kx + (L, N), tdt, dev)
-    _check(C, "C", (Bsz,) + kx + (L, N), tdt, dev)
-    _check(z, "z", (Bsz, L, Dm), tdt, dev)
-    _check(A, "A", kx + (Dm, N), torch.float32, dev)
-    _check(D, "D", kx + (Dm,), torch.float32, dev)
-    _check(delta_bias, "delta_bias", kx + (Dm,), torch.float32, dev)
-    _check(initial_state, "initial_state", (Bsz,) + kx + (Dm, N), torch.float32, dev)
+    _check_fwd_shapes(u, delta, A, B, C, D, z, delta_bias, initial_state, dir_mode, K, Bsz, L, Dm, N, tdt, dev)
     if out is None:
         out = torch.empty((Bsz, L, Dm), dtype=tdt, device=dev)
     _check(out, "out", (Bsz, L, Dm), tdt, dev)

@@ -9,9 +9,24 @@
 #include "conv_kernels.h"
 #include "scan_launch.h"
 
+#include <mutex>
+
 using namespace mscan;
 
+// Scratch of mamba_scan_fwd_noalloc: the workspace it would otherwise take from
+// the caller (per-direction rows, time-split carries), as one static device
+// array.  Each device the library runs on holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// array: host code only ever uses the address that hipGetSymbolAddress returns
+// for the device (scratch_of_stream below).
+constexpr size_t kScratchBytes = MAMBA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+char* g_scratch[kScratchDevices];  // device address of `scratch` per device, once looked up
 
 int num_dirs(int mode) { return mode == MAMBA_DIR_BIDIR ? 2 : mode == MAMBA_DIR_CROSS2D ? 4 : 1; }
 
@@ -296,6 +311,58 @@ int saved_layout(const mamba_dims* g, int mode, bool rows, SavedLayout* s) {
   return MAMBA_OK;
 }
 
+// Validation shared by the forward entry points (pointers, alignment, plan).
+int check_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+              const void* z, const float* delta_bias, const mamba_dims* dims, int dir_mode, const void* out,
+              const float* last_state, Plan* pl) {
+  const int rc = make_plan(dims, dir_mode, pl);
+  if (rc != MAMBA_OK) return rc;
+  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID;
+  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, out, last_state, dims->initial_state};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
+  return MAMBA_OK;
+}
+
+// The forward pass with its workspace at ws (pl.total() bytes, or none).
+int run_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
+            const void* z, const float* delta_bias, const mamba_dims* dims, int dir_mode, void* out,
+            float* last_state, const Plan& pl, char* ws, hipStream_t stream) {
+  ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
+  p.out = out;
+  p.ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
+  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
+  p.last_state = last_state;
+  return dispatch_fwd(dims, p, pl, stream);
+}
+
+// Device address of the static scratch on the device of `stream` (the
+// current device for the null stream), looked up once per device with that
+// device current and kept for the life of the process.
+int scratch_of_stream(hipStream_t stream, char** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return MAMBA_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return MAMBA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kScratchDevices) return MAMBA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return MAMBA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return MAMBA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return MAMBA_ERR_HIP;
+    if (e != hipSuccess || ptr == nullptr) return MAMBA_ERR_HIP;
+    g_scratch[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return MAMBA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -310,24 +377,29 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A, const void*
                    const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
                    int dir_mode, void* out, float* last_state, hipStream_t stream) {
   Plan pl;
-  const int rc = make_plan(dims, dir_mode, &pl);
+  const int rc = check_fwd(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, out, last_state, &pl);
   if (rc != MAMBA_OK) return rc;
-  if (!u || !delta || !A || !B || !C || !out) return MAMBA_ERR_INVALID;
-  const void* ptrs[] = {u, delta, A, B, C, D, z, delta_bias, out, last_state, dims->initial_state};
-  for (const void* q : ptrs)
-    if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;
   const size_t need = pl.total();
   if (need > 0 && (!dims->workspace || dims->workspace_bytes < need || !aligned16(dims->workspace)))
     return MAMBA_ERR_WORKSPACE;
+  return run_fwd(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, out, last_state, pl,
+                 static_cast<char*>(dims->workspace), stream);
+}
 
-  ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
-  p.out = out;
-  char* ws = static_cast<char*>(dims->workspace);
-  p.ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
-  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
-  p.last_state = last_state;
-  return dispatch_fwd(dims, p, pl, stream);
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
+                           int dir_mode, void* out, float* last_state, hipStream_t stream) {
+  Plan pl;
+  int rc = check_fwd(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, out, last_state, &pl);
+  if (rc != MAMBA_OK) return rc;
+  const size_t need = pl.total();
+  if (need > kScratchBytes) return MAMBA_ERR_SCRATCH;
+  char* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_of_stream(stream, &ws);
+    if (rc != MAMBA_OK) return rc;
+  }
+  return run_fwd(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, out, last_state, pl, ws, stream);
 }
 
 size_t mamba_scan_saved_bytes(const mamba_dims* dims, int dir_mode, int gated) {
@@ -536,6 +608,7 @@ const char* mamba_status_string(int status) {
     case MAMBA_ERR_UNSUPPORTED: return "unsupported (state size, channel count, alignment or size limit)";
     case MAMBA_ERR_WORKSPACE: return "workspace missing or smaller than the *_workspace_bytes() figure";
     case MAMBA_ERR_HIP: return "HIP runtime rejected a kernel launch";
+    case MAMBA_ERR_SCRATCH: return "mamba_scan_fwd_noalloc: the problem needs more than the library's 32 MiB static scratch";
     default: return "unknown status";
   }
 }

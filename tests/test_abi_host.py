@@ -47,7 +47,7 @@ def test_exports_nothing_else(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert len(ms.status_string(code)) > 0
     assert ms.status_string(0) == "ok"
 
@@ -239,3 +239,32 @@ def test_bench_refuses_several_gpus():
         assert r.returncode == 2, (args, env, r.returncode)
         assert "measures one GPU" in r.stderr
         assert r.stdout == ""
+
+
+def test_fwd_noalloc_validation(lib):
+    """mamba_scan_fwd_noalloc validates like mamba_scan_fwd, ignores the dims'
+    workspace, and refuses (before any GPU work) a problem whose scratch would
+    not fit the library's static array."""
+    E = ms._binding
+
+    def call(d, mode=ms.DIR_FWD, **ptrs):
+        p = dict(u=FAKE, delta=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, z=None, bias=None, out=FAKE, last=None)
+        p.update(ptrs)
+        return lib.mamba_scan_fwd_noalloc(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["bias"],
+                                          ctypes.byref(d), mode, p["out"], p["last"], None)
+    assert call(dims(), u=None) == E.MAMBA_ERR_INVALID
+    assert call(dims(batch=0)) == E.MAMBA_ERR_INVALID
+    assert call(dims(), mode=9) == E.MAMBA_ERR_INVALID
+    assert call(dims(dim=60)) == E.MAMBA_ERR_UNSUPPORTED
+    assert call(dims(), u=FAKE + 4) == E.MAMBA_ERR_UNSUPPORTED
+    # the scratch limit: per-direction fp32 rows of a bidirectional scan, K*B*L*D*4 bytes
+    cap = E.NOALLOC_SCRATCH_BYTES
+    big = dims(batch=1, dim=1024, seqlen=cap // (2 * 1024 * 4) + 64)
+    assert ms.workspace_bytes(big, ms.DIR_BIDIR) > cap
+    assert call(big, mode=ms.DIR_BIDIR) == E.MAMBA_ERR_SCRATCH
+    # the workspace fields are ignored: a workspace that mamba_scan_fwd would
+    # accept does not lift the limit
+    need = ms.workspace_bytes(big, ms.DIR_BIDIR)
+    big.workspace, big.workspace_bytes = FAKE, need
+    assert call(big, mode=ms.DIR_BIDIR) == E.MAMBA_ERR_SCRATCH
+    assert "static scratch" in ms.status_string(E.MAMBA_ERR_SCRATCH)
