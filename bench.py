@@ -34,10 +34,14 @@ sys.path.insert(0, ROOT)
 # Vector-ALU peak of MI355X (gfx950) for this method.  The published fp32 vector
 # rate, 157.3 TFLOP/s, is 78.6e12 fp32 lane-operations/s (an FMA counts two flops):
 # 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz, one 64-lane fp32 add/mul/FMA per 2 cycles
-# per SIMD, which is what these instructions measure on the chip.  v_exp_f32 issues
-# at a quarter of that rate (measured: 8 cycles per 64-lane instruction).  Each
-# scan element needs four fp32 operations (Δ'·A, Δu·B, the state FMA, the readout
-# FMA) and one exp: 4/78.6e12 + 1/19.7e12 s, i.e. 9.83e12 elements/s.
+# per SIMD.  v_exp_f32 issues at a quarter of that rate (8 lanes per cycle per
+# SIMD).  Each scan element needs four fp32 operations (Δ'·A, Δu·B, the state FMA,
+# the readout FMA) and one exp: 4/78.6e12 + 1/19.7e12 s, i.e. 9.83e12 elements/s.
+# Measured on the chip with a warmed-up clock (2.2-2.4 GHz under load), 8 waves per
+# SIMD, register-only loops: VOP2 fp32 instructions 2.6 cycles each, VOP3 v_fma_f32
+# 4.4, v_exp_f32 about 10, v_permlane32_swap about 10; the bare recurrence (the
+# five instructions per element) 20-22 cycles per 64 elements, about 75 % of this
+# peak.
 FP32_LANE_OPS = 256 * 4 * 32 * 2.4e9
 EXP_LANE_OPS = FP32_LANE_OPS / 4
 ALU_PEAK_ELEM = 1.0 / (4.0 / FP32_LANE_OPS + 1.0 / EXP_LANE_OPS)
@@ -108,25 +112,33 @@ def measured_traffic(workload: str):
     return int(rec["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(w, budget_s: float = 15.0):
-    """Time the fp64 oracle on a bounded sample of the workload's (b, d) rows."""
+def cpu_baseline(w, x=None, budget_s: float = 15.0, sample_note: str = ""):
+    """Time the fp64 oracle on a bounded sample of the workload's (b, d) rows
+    (drawn without replacement).  x: host inputs of w (make_inputs layout);
+    drawn here when None.  w.dim may be a channel subset of the named workload
+    (sample_note says which)."""
     import oracle
     from selective_state_space_mamba_amd import inputs as I
-    x = I.make_inputs(w)
+    if x is None:
+        x = I.make_inputs(w)
     threads = min(16, os.cpu_count() or 1)
     rng = np.random.Generator(np.random.PCG64(3))
-    # calibrate on a few rows, then size the sample to about `budget_s`
-    rows = np.stack([rng.integers(0, w.batch, 64), rng.integers(0, w.dim, 64)], axis=1)
-    t0 = time.perf_counter()
-    oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
-                dir_mode=w.dir_mode, height=w.height, width=w.width, rows=rows, nthreads=threads)
-    per_row = (time.perf_counter() - t0) / 64
-    n = int(min(w.batch * w.dim, max(64, budget_s / max(per_row, 1e-9))))
-    rows = np.stack([rng.integers(0, w.batch, n), rng.integers(0, w.dim, n)], axis=1)
+    total = w.batch * w.dim
+
+    def pick(n):
+        flat = np.sort(rng.choice(total, size=min(n, total), replace=False))
+        return np.stack([flat // w.dim, flat % w.dim], axis=1).astype(np.int64)
 
     def run(r, nthreads):
         oracle.scan(x["u"], x["delta"], x["A"], x["B"], x["C"], x["D"], x["z"], x["delta_bias"],
                     dir_mode=w.dir_mode, height=w.height, width=w.width, rows=r, nthreads=nthreads)
+    # calibrate on a few rows, then size the sample to about budget_s / 3 per pass
+    cal = pick(min(64, total))
+    t0 = time.perf_counter()
+    run(cal, threads)
+    per_row = (time.perf_counter() - t0) / len(cal)
+    n = int(min(total, max(len(cal), budget_s / 3 / max(per_row, 1e-9))))
+    rows = pick(n)
     # passes over the sample until about budget_s / 3 seconds (a sample that
     # is the whole workload may take well under a second)
     t0 = time.perf_counter()
@@ -138,18 +150,152 @@ def cpu_baseline(w, budget_s: float = 15.0):
         if dt >= budget_s / 3 or passes >= 100:
             break
     el = passes * n * w.ndirs * w.seqlen * w.dstate
-    # one thread, on a sample sized to about budget_s / 5 seconds
-    n1 = int(min(n, max(16, budget_s / 5 / max(per_row * threads, 1e-9))))
+    # one thread, on the first rows of the sample, about budget_s / 5 seconds
+    n1 = int(min(n, max(1, budget_s / 5 / max(per_row * threads, 1e-9))))
     t0 = time.perf_counter()
     run(rows[:n1], 1)
     dt1 = time.perf_counter() - t0
     el1 = n1 * w.ndirs * w.seqlen * w.dstate
     return {"value": el / dt, "unit": "scan elements/s", "cores": threads, "kind": "oracle",
-            "sample": "%d of %d (b, d) rows of %s, all %d tokens and %d states, fp64, %d passes in %.1f s"
-                      % (n, w.batch * w.dim, w.name, w.seqlen, w.dstate, passes, dt),
+            "sample": "%d distinct (b, d) rows of %d%s of %s, all %d tokens, %d states and %d directions, fp64, "
+                      "%d passes in %.1f s" % (n, total, sample_note, w.name, w.seqlen, w.dstate, w.ndirs, passes, dt),
             "nproc": os.cpu_count(),
             "single_thread": {"value": el1 / dt1, "unit": "scan elements/s",
-                              "sample": "%d rows, %.1f s" % (n1, dt1)}}
+                              "sample": "%d of those rows, %.1f s" % (n1, dt1)}}
+
+
+def decode_cpu_baseline(x, steps: int, budget_s: float = 3.0):
+    """Time the oracle's one-token step over every (b, d) row (single thread)."""
+    import oracle
+    st = np.zeros((x["B"].shape[0], x["A"].shape[-2], x["A"].shape[-1]), dtype=np.float64)
+    t0 = time.perf_counter()
+    done = 0
+    while done < steps:
+        oracle.step(st, x["u"][:, done], x["delta"][:, done], x["A"], x["B"][:, done], x["C"][:, done], x["D"],
+                    None if x["z"] is None else x["z"][:, done], x["delta_bias"])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"us_per_step": dt * 1e6 / done, "steps": done, "cores": 1, "kind": "oracle",
+            "sample": "%d steps over all %d (b, d) rows, fp64" % (done, st.shape[0] * st.shape[1])}
+
+
+class Timer:
+    """Per-launch durations with HIP events recorded on the launch stream."""
+
+    def __init__(self, torch, stream, n):
+        self.torch, self.stream = torch, stream
+        self.evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def run(self, fn, n):
+        for i in range(n):
+            self.evs[i][0].record(self.stream)
+            fn(i)
+            self.evs[i][1].record(self.stream)
+
+    def ms(self, n):
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in self.evs[:n]]
+
+
+def warm_up(torch, stream, fn, min_calls: int, min_gpu_ms: float):
+    """At least min_calls calls, and more until min_gpu_ms of GPU time has run
+    (the clocks need some tens of milliseconds of work to settle).  Returns
+    (calls, gpu_ms)."""
+    calls, gpu_ms = 0, 0.0
+    while calls < min_calls or gpu_ms < min_gpu_ms:
+        n = max(1, min_calls - calls) if calls < min_calls else max(1, calls // 2)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(calls + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gpu_ms += e0.elapsed_time(e1)
+        calls += n
+        if calls > 100000:
+            break
+    return calls, gpu_ms
+
+
+def copy_ceiling(torch, stream, nbytes: int, reps: int = 10):
+    """Rate of torch's device copy moving `nbytes` per call (nbytes/2 read and
+    nbytes/2 written), over three rotating buffer pairs so that the 256 MB
+    Infinity Cache cannot serve it."""
+    half = max(1 << 20, nbytes // 2) // 16 * 16
+    pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda:0"),
+              torch.empty(half, dtype=torch.uint8, device="cuda:0")) for _ in range(3)]
+    for a, b in pairs:
+        a.fill_(1)
+    with torch.cuda.stream(stream):
+        for i in range(6):
+            pairs[i % 3][1].copy_(pairs[i % 3][0])
+        t = Timer(torch, stream, reps)
+        t.run(lambda i: pairs[i % 3][1].copy_(pairs[i % 3][0]), reps)
+        ms = t.ms(reps)
+    del pairs
+    s = float(np.mean(ms)) * 1e-3
+    return {"op": "torch device copy, %d bytes read + %d written per call" % (half, half),
+            "us_per_call": s * 1e6, "gbs": 2 * half / s / 1e9, "frac_of_peak": 2 * half / s / 1e9 / HBM_PEAK_GBS}
+
+
+def time_config(torch, ms, I, w, steps: int, warm_ms: float, stream, cpu: bool):
+    """One forward workload at full size: inputs drawn on the GPU (enough sets
+    to exceed the Infinity Cache), per-launch HIP-event timing after a warm-up
+    of at least warm_ms of GPU time, the rooflines, a copy ceiling of the same
+    byte count, and the oracle on a channel sample."""
+    dev = torch.device("cuda:0")
+    alg = algorithmic_bytes(w)
+    nsets = max(1, min(3, -(-600_000_000 // alg)))
+    sets = [I.make_inputs_device(w, dev, seed=w.seed + 1000 * s_) for s_ in range(nsets)]
+    K = w.ndirs
+    kx = () if K == 1 else (K,)
+    outs = [torch.empty((w.batch, w.seqlen, w.dim), dtype=sets[0]["u"].dtype, device=dev) for _ in sets]
+    states = [torch.empty((w.batch,) + kx + (w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in sets]
+    dims = ms.make_dims(w.batch, w.dim, w.seqlen, w.dstate, ms.DTYPE_BF16 if w.dtype == "bf16" else ms.DTYPE_F32,
+                        height=w.height, width=w.width)
+    ws = torch.empty(max(ms.workspace_bytes(dims, w.dir_mode), 256), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s_ = sets[i % nsets]
+        ms.scan_fwd(s_["u"], s_["delta"], s_["A"], s_["B"], s_["C"], s_["D"], s_["z"], s_["delta_bias"],
+                    dir_mode=w.dir_mode, height=w.height, width=w.width, out=outs[i % nsets],
+                    last_state=states[i % nsets], workspace=ws, stream=stream)
+    with torch.cuda.stream(stream):
+        wcalls, wms = warm_up(torch, stream, step, 2, warm_ms)
+        t = Timer(torch, stream, steps)
+        t.run(step, steps)
+        launch_ms = t.ms(steps)
+    avg = float(np.mean(launch_ms)) * 1e-3
+    el = w.elements
+    rec = {"config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
+                      "dir_mode": ["fwd", "bwd", "bidir", "cross2d"][w.dir_mode], "gated": w.gated,
+                      "height": w.height, "width": w.width, "dtype": w.dtype},
+           "calls": steps, "input_sets": nsets, "warmup_calls": wcalls, "warmup_gpu_ms": wms,
+           "us_per_call": avg * 1e6, "median_us": float(np.median(launch_ms)) * 1e3,
+           "min_us": float(np.min(launch_ms)) * 1e3, "elements": el, "elements_per_s": el / avg,
+           "alu_frac": el / avg / ALU_PEAK_ELEM, "algorithmic_bytes": alg, "hbm_gbs": alg / avg / 1e9,
+           "hbm_frac": alg / avg / 1e9 / HBM_PEAK_GBS, "workspace_bytes": int(ws.numel()),
+           "traffic": measured_traffic(w.name)}
+    rec["copy_ceiling"] = copy_ceiling(torch, stream, alg)
+    if cpu:
+        # a channel sample: every batch, direction and token of 2 to 256 channels,
+        # about a million oracle rows x tokens at most
+        nch = int(max(2, min(256, w.dim, 4_000_000 // max(1, w.batch * w.seqlen))))
+        chans = np.sort(np.random.Generator(np.random.PCG64(5)).choice(w.dim, size=nch, replace=False))
+        xs = I.host_channel_sample(w, sets[0], chans)
+        rec["cpu_baseline"] = cpu_baseline(w.with_(dim=nch), xs, budget_s=9.0,
+                                           sample_note=" (channels %s of %d, drawn on the GPU)"
+                                           % (_span(chans), w.dim))
+    del sets, outs, states, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def _span(ch):
+    return "%d..%d, %d of them" % (int(ch[0]), int(ch[-1]), len(ch))
 
 
 def main():
@@ -160,6 +306,10 @@ def main():
     # after 5 warm-up calls (~1 ms) the next 50 forward calls of the 130M layer
     # ran 7 % slower than the 50 after them
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup-ms", type=float, default=250.0,
+                    help="keep warming up until this much GPU time has run, whatever --warmup says")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed calls of each of the other specified workloads (0: skip them)")
     ap.add_argument("--workload", default="mamba130m_layer")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps (defeats the 256 MB MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -195,8 +345,11 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(v)).to(dev)
 
     sets = []
+    host0 = None
     for s in range(args.sets):
         x = I.make_inputs(w.with_(seed=w.seed + 1000 * s))
+        if s == 0:
+            host0 = x
         sets.append({k: todev(v) for k, v in x.items()})
     K = w.ndirs
     kx = () if K == 1 else (K,)
@@ -214,23 +367,19 @@ def main():
                     last_state=states[i % len(sets)], workspace=ws, stream=stream)
 
     with torch.cuda.stream(stream):
-        for i in range(args.warmup):
-            step(i)
+        # the W warm-up calls asked for, and more until the GPU has run at
+        # least --warmup-ms of this work (its clocks settle after some tens of
+        # milliseconds)
+        warm_calls, warm_ms = warm_up(torch, stream, step, args.warmup, args.warmup_ms)
         torch.cuda.synchronize()
-        # timed region: the whole step sequence, wall clock around synchronisations
+        # timed region: exactly K steps, wall clock around synchronisations,
+        # with a HIP event pair on the launch stream around each launch
+        timer = Timer(torch, stream, args.steps)
         t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(i)
+        timer.run(step, args.steps)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        # per-launch durations with HIP events on the launch stream
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for i in range(args.steps):
-            evs[i][0].record(stream)
-            step(i)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        launch_ms = [a.elapsed_time(b) for a, b in evs]
+        launch_ms = timer.ms(args.steps)
 
     ms_step = wall * 1e3 / args.steps
     el = w.elements
@@ -279,7 +428,9 @@ def main():
         del graph
         decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
                   "graph_us_per_step": gdec_s * 1e6 / args.decode_steps,
-                  "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4}
+                  "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4,
+                  "elements_per_step": w.batch * w.dim * w.dstate,
+                  "cpu_baseline": None if args.no_cpu_baseline else decode_cpu_baseline(host0, args.decode_steps)}
 
     conv = None
     if args.conv_steps > 0 and w.dir_mode == 0:
@@ -426,7 +577,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    copy = copy_ceiling(torch, stream, alg_bytes)
+    del sets, outs, states, ws
+    torch.cuda.empty_cache()
+    configs = {}
+    if args.config_steps > 0:
+        for name in ("long_context", "vim_bidir_224", "vim_bidir_1248", "vmamba_ss2d"):
+            if name == w.name:
+                continue
+            wc = I.WORKLOADS[name]
+            print("[bench] %s" % name, file=sys.stderr, flush=True)
+            configs[name] = time_config(torch, ms, I, wc, max(5, args.config_steps if name != "long_context"
+                                                              else args.config_steps // 4),
+                                        args.warmup_ms, stream, not args.no_cpu_baseline)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, host0)
     rec = {
         "metric": "scan elements (B*D*L*N)/s, selective scan forward, bf16 L=2048 D=1536 N=16",
         "value": value,
@@ -434,12 +598,14 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_calls_run": warm_calls,
+        "warmup_gpu_ms": warm_ms,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) inputs, S4D-real A, %d input sets rotated)" % len(sets),
+        "data": "synthetic (seeded N(0,1) inputs, S4D-real A, %d input sets rotated)" % args.sets,
         "config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                    "dir_mode": ["fwd", "bwd", "bidir", "cross2d"][w.dir_mode], "gated": w.gated,
                    "state_dtype": "f32", "parallelism": "single GPU"},
@@ -451,12 +617,13 @@ def main():
                      "kernel_median_us": float(np.median(launch_ms)) * 1e3,
                      "kernel_min_us": float(np.min(launch_ms)) * 1e3,
                      "hbm": {"achieved": hbm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": hbm_gbs / HBM_PEAK_GBS,
-                             "algorithmic_bytes": alg_bytes}},
+                             "algorithmic_bytes": alg_bytes, "copy_ceiling": copy}},
         "cpu_baseline": cpu,
         "decode": decode,
         "conv1d": conv,
         "backward": bwd,
         "variants": variants,
+        "configs": configs,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)

@@ -1,6 +1,7 @@
 """Builds libmamba_scan.so (the gfx950 HIP kernels and their C ABI) in-tree.
 
-The kernels are instantiated in four translation units (element type x
+The kernels are instantiated in eight translation units (the channel-block,
+step and backward kernels, and the row kernels; each per element type x
 input-term rule) compiled in parallel next to the host layer, then linked.
 """
 from __future__ import annotations
@@ -17,8 +18,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmamba_scan.so")
 HOST = os.path.join(CSRC, "mamba_scan.hip")
 INST = os.path.join(CSRC, "scan_inst.hip")
-SOURCES = [HOST, INST]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("scan_launch.h", "scan_kernels.h", "scan_bwd.h", "conv_kernels.h",
+ROWS = os.path.join(CSRC, "row_inst.hip")
+SOURCES = [HOST, INST, ROWS]
+DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("scan_launch.h", "scan_kernels.h", "scan_row.h", "scan_bwd.h", "conv_kernels.h",
                                                   "device_math.h")] + [
     os.path.join(ROOT, "include", "mamba_scan.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -45,10 +47,11 @@ def build(force: bool = True, extra_flags=(), out: str | None = None) -> str:
         return out
     with tempfile.TemporaryDirectory(prefix="mscan_build_") as tmp:
         jobs = [[HIPCC] + FLAGS + list(extra_flags) + ["-c", "-o", os.path.join(tmp, "host.o"), HOST]]
-        for bf16, exact in VARIANTS:
-            obj = os.path.join(tmp, "inst_%d%d.o" % (bf16, exact))
-            jobs.append([HIPCC] + FLAGS + list(extra_flags) +
-                        ["-DMSCAN_INST_BF16=%d" % bf16, "-DMSCAN_INST_EXACT=%d" % exact, "-c", "-o", obj, INST])
+        for unit in (INST, ROWS):
+            for bf16, exact in VARIANTS:
+                obj = os.path.join(tmp, "%s_%d%d.o" % (os.path.basename(unit).split(".")[0], bf16, exact))
+                jobs.append([HIPCC] + FLAGS + list(extra_flags) +
+                            ["-DMSCAN_INST_BF16=%d" % bf16, "-DMSCAN_INST_EXACT=%d" % exact, "-c", "-o", obj, unit])
         with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
             list(ex.map(_run, jobs))
         objs = [j[j.index("-o") + 1] for j in jobs]

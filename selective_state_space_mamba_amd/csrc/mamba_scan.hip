@@ -42,6 +42,63 @@ int kinds_of(int mode) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+#ifndef MSCAN_FORCE_KERNEL
+#define MSCAN_FORCE_KERNEL 0  // 1: the channel-block kernel wherever it applies, 2: the row kernel everywhere
+#endif
+#ifndef MSCAN_ROW_MIN_CHUNK
+#define MSCAN_ROW_MIN_CHUNK 256  // shortest time chunk of the row kernel's split
+#endif
+
+// Which forward kernel: scan_row_kernel (one channel per lane, every state in
+// its registers) or scan_chunk_kernel (channel blocks with the states spread
+// over lanes).  Only the row kernel takes state sizes that are not a power of
+// two and channel counts that are not a multiple of 8.
+bool choose_rows(const mamba_dims* g, int K) {
+  const int64_t N = g->dstate;
+  if ((N & (N - 1)) != 0 || g->dim % 8 != 0) return true;
+  if (MSCAN_FORCE_KERNEL == 1) return false;
+  if (MSCAN_FORCE_KERNEL == 2) return true;
+  // The row kernel (rows of 64 channels, one wave each) also serves a single
+  // direction whose channel blocks are too few to fill the GPU, where both
+  // kernels split the sequence in time.  Measured on MI355X (row vs channel
+  // block, µs): the 262k-token context 3997 vs 4150; elsewhere it loses --
+  // 130M layer 253 vs 142, Vim-224 217 vs 208, 97k-token Vim 1322 vs 1253,
+  // SS2D 910 vs 634.
+  const int64_t blk_waves = (int64_t)K * g->batch * ((g->dim + 15) / 16) * (N < 4 ? 1 : N) / 4;
+  return K == 1 && blk_waves < MSCAN_TARGET_WAVES / 2 && g->seqlen >= 2 * MSCAN_MIN_CHUNK;
+}
+
+// Launch plan of the row kernel: 64 channels per wave, split in time into
+// enough chunks for ~MSCAN_TARGET_WAVES waves when the rows are fewer.
+int plan_rows(const mamba_dims* g, int K, Plan* pl) {
+  const int64_t L = g->seqlen, N = g->dstate;
+  pl->row = 1;
+  pl->cb = 64;
+  pl->g = (int)N;
+  pl->prio = 0;
+  pl->nblk_d = (int)((g->dim + 63) / 64);
+  const int64_t rows = (int64_t)K * g->batch * pl->nblk_d;
+  int64_t nch = 1;
+  if (rows < MSCAN_TARGET_WAVES) {
+    nch = (MSCAN_TARGET_WAVES + rows - 1) / rows;
+    if (nch > L / MSCAN_ROW_MIN_CHUNK) nch = L / MSCAN_ROW_MIN_CHUNK;
+    if (nch > MSCAN_MAX_CHUNKS) nch = MSCAN_MAX_CHUNKS;
+    if (nch < 1) nch = 1;
+  }
+  if (MSCAN_FORCE_CHUNKS > 0) nch = MSCAN_FORCE_CHUNKS < L ? MSCAN_FORCE_CHUNKS : L;
+  const int64_t clen = (L + nch - 1) / nch;
+  nch = (L + clen - 1) / clen;
+  if (pl->nblk_d * nch * g->batch * K > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
+  pl->nchunks = (int)nch;
+  pl->chunk_len = (int)clen;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  pl->ws_y_bytes = K > 1 ? up((size_t)K * g->batch * L * g->dim * sizeof(float)) : 0;
+  pl->agg_state_bytes = nch > 1 ? up((size_t)K * g->batch * (nch - 1) * g->dim * N * sizeof(float)) : 0;
+  pl->agg_dsum_bytes = nch > 1 ? up((size_t)K * g->batch * (nch - 1) * g->dim * sizeof(float)) : 0;
+  pl->bc_bytes = up(2 * ((size_t)K * g->batch * L + 2) * pl->np * sizeof(float));  // B, C: rows + 2 padding rows each
+  return MAMBA_OK;
+}
+
 // Validates the sizes (no pointers) and derives the launch plan.  A pure
 // function of dims and mode.
 int make_plan(const mamba_dims* g, int mode, Plan* pl) {
@@ -54,8 +111,8 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
        g->height * g->width != g->seqlen))
     return MAMBA_ERR_INVALID;
   const int64_t N = g->dstate;
-  if (N > 64 || (N & (N - 1)) != 0) return MAMBA_ERR_UNSUPPORTED;
-  if (g->dim % 8 != 0) return MAMBA_ERR_UNSUPPORTED;
+  if (N > 64) return MAMBA_ERR_UNSUPPORTED;
+  if (g->dim % (g->dtype == MAMBA_DTYPE_BF16 ? 8 : 4) != 0) return MAMBA_ERR_UNSUPPORTED;
   const int K = num_dirs(mode);
   // token and grid indices are 32-bit inside the kernels; element offsets are 64-bit
   if (g->seqlen > INT32_MAX / 2 || g->dim > INT32_MAX / 2 || g->batch > INT32_MAX / 8 ||
@@ -85,6 +142,11 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   // into enough chunks for ~24 waves per SIMD (32 -> 48 or 64 chunks: -2 to
   // -3 % on the long workloads).
   const int64_t L = g->seqlen;
+  pl->np = 1;
+  while (pl->np < N) pl->np *= 2;
+  if (choose_rows(g, K)) return plan_rows(g, K, pl);
+  pl->row = 0;
+  pl->bc_bytes = 0;
   const int cb = layout_of((int)N).cb;
   const int64_t rows = (int64_t)K * g->batch * ((g->dim + cb - 1) / cb);
   // 2 states per thread at N = 16 when there are waves to spare, or when the
@@ -153,7 +215,7 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const int rc = make_plan(g, mode, &bp->fwd);
   if (rc != MAMBA_OK) return rc;
   // one state per thread and 32-position checkpoints (the forward tile)
-  if (g->dstate > 16 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  if (g->dstate > 16 || (g->dstate & (g->dstate - 1)) != 0 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
   // the recompute always keeps per-direction fp32 rows (32-bit slice offsets)
   if (g->seqlen * g->dim * 4 > ((int64_t)1 << 31)) return MAMBA_ERR_UNSUPPORTED;
   const Plan& pl = bp->fwd;
@@ -184,7 +246,7 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
     off += up(bytes);
     return at;
   };
-  bp->agg = take(pl.agg_state_bytes + pl.agg_dsum_bytes);
+  bp->agg = take(pl.agg_state_bytes + pl.agg_dsum_bytes + pl.bc_bytes);
   bp->ws_y = take((size_t)K * Bz * L * Dm * f4);
   bp->ckpt = take((size_t)K * Bz * bp->ntiles * Dm * N * f4);
   bp->dB = take((size_t)bp->nblk * Bz * K * L * N * f4);
@@ -273,6 +335,7 @@ ScanParams scan_params(const void* u, const void* delta, const float* A, const v
   p.L = (int)dims->seqlen;
   p.H = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->height : 1;
   p.W = dir_mode == MAMBA_DIR_CROSS2D ? (int)dims->width : (int)dims->seqlen;
+  p.N = (int)dims->dstate;
   p.K = pl.K;
   p.Ku = pl.Ku;
   p.kinds = kinds_of(dir_mode);
@@ -285,6 +348,11 @@ ScanParams scan_params(const void* u, const void* delta, const float* A, const v
 
 int dispatch_fwd(const mamba_dims* dims, const ScanParams& p, const Plan& pl, hipStream_t stream) {
   const bool exact = dims->exact_zoh != 0;
+  if (pl.row) {
+    if (dims->dtype == MAMBA_DTYPE_BF16)
+      return exact ? dispatch_rows_bf16_exact(p, pl, stream) : dispatch_rows_bf16_simple(p, pl, stream);
+    return exact ? dispatch_rows_f32_exact(p, pl, stream) : dispatch_rows_f32_simple(p, pl, stream);
+  }
   if (dims->dtype == MAMBA_DTYPE_BF16)
     return exact ? dispatch_scan_bf16_exact(dims->dstate, p, pl, stream)
                  : dispatch_scan_bf16_simple(dims->dstate, p, pl, stream);
@@ -311,6 +379,20 @@ int saved_layout(const mamba_dims* g, int mode, bool rows, SavedLayout* s) {
   return MAMBA_OK;
 }
 
+// Points the forward pass's scratch regions into a workspace laid out as Plan
+// describes: the per-direction rows at ws (when rows is true), the other
+// regions from rest on (ws + pl.ws_y_bytes in a whole forward workspace).
+void set_workspace(ScanParams* p, const Plan& pl, char* ws, bool rows, char* rest) {
+  if (rows) p->ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  char* w = rest;
+  size_t off = 0;
+  p->agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(w + off) : nullptr;
+  off += pl.agg_state_bytes;
+  p->agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(w + off) : nullptr;
+  off += pl.agg_dsum_bytes;
+  p->bcw = pl.bc_bytes ? reinterpret_cast<float*>(w + off) : nullptr;
+}
+
 // Validation shared by the forward entry points (pointers, alignment, plan).
 int check_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C, const float* D,
               const void* z, const float* delta_bias, const mamba_dims* dims, int dir_mode, const void* out,
@@ -330,9 +412,7 @@ int run_fwd(const void* u, const void* delta, const float* A, const void* B, con
             float* last_state, const Plan& pl, char* ws, hipStream_t stream) {
   ScanParams p = scan_params(u, delta, A, B, C, D, z, delta_bias, dims, dir_mode, pl);
   p.out = out;
-  p.ws_y = pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
-  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
+  set_workspace(&p, pl, ws, true, ws + pl.ws_y_bytes);
   p.last_state = last_state;
   return dispatch_fwd(dims, p, pl, stream);
 }
@@ -431,9 +511,8 @@ int mamba_scan_fwd_save(const void* u, const void* delta, const float* A, const 
   char* sv = static_cast<char*>(saved);
   // gated: the per-direction rows go to the saved buffer (the merge reads
   // them there); ungated with several directions: to the workspace as usual
-  p.ws_y = z ? reinterpret_cast<float*>(sv + sl.rows) : (pl.ws_y_bytes ? reinterpret_cast<float*>(ws) : nullptr);
-  p.agg_state = pl.agg_state_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes) : nullptr;
-  p.agg_dsum = pl.agg_dsum_bytes ? reinterpret_cast<float*>(ws + pl.ws_y_bytes + pl.agg_state_bytes) : nullptr;
+  set_workspace(&p, pl, ws, true, ws + pl.ws_y_bytes);
+  if (z) p.ws_y = reinterpret_cast<float*>(sv + sl.rows);
   p.last_state = last_state;
   p.ckpt = reinterpret_cast<float*>(sv);
   p.ckpt_tiles = sl.bp.ntiles;
@@ -479,8 +558,9 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   } else {
     p.out = nullptr;
     p.ws_y = (z && dz) ? wsf(bp.ws_y) : nullptr;  // the rows serve dz alone
-    p.agg_state = pl.agg_state_bytes ? wsf(bp.agg) : nullptr;
-    p.agg_dsum = pl.agg_dsum_bytes ? wsf(bp.agg + pl.agg_state_bytes) : nullptr;
+    // the forward plan's split carries and B/C copies at bp.agg (its rows
+    // region, unused here, is left out of the reservation)
+    set_workspace(&p, pl, nullptr, false, ws + bp.agg);
     p.last_state = nullptr;
     p.ckpt = wsf(bp.ckpt);
     p.ckpt_tiles = bp.ntiles;
@@ -572,8 +652,9 @@ int mamba_scan_step(float* state, const void* u_t, const void* delta_t, const fl
   if (dims->dtype != MAMBA_DTYPE_F32 && dims->dtype != MAMBA_DTYPE_BF16) return MAMBA_ERR_INVALID;
   if (dims->batch <= 0 || dims->dim <= 0 || dims->dstate <= 0) return MAMBA_ERR_INVALID;
   const int64_t N = dims->dstate;
-  if (N > 64 || (N & (N - 1)) != 0) return MAMBA_ERR_UNSUPPORTED;
-  if (dims->dim % 8 != 0 || dims->batch * dims->dim > INT32_MAX / 64) return MAMBA_ERR_UNSUPPORTED;
+  if (N > 64) return MAMBA_ERR_UNSUPPORTED;
+  if (dims->dim % (dims->dtype == MAMBA_DTYPE_BF16 ? 8 : 4) != 0 || dims->batch * dims->dim > INT32_MAX / 64)
+    return MAMBA_ERR_UNSUPPORTED;
   const void* ptrs[] = {state, u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, out};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MAMBA_ERR_UNSUPPORTED;

@@ -68,7 +68,9 @@ struct ScanParams {
   float* agg_state;         // [K][Bsz][nchunks-1][D][N]
   float* agg_dsum;          // [K][Bsz][nchunks-1][D]
   float* ckpt;              // [K][Bsz][ckpt_tiles][D][N] state at every tile start, or null
+  float* bcw;               // row kernel: B then C widened to fp32 rows of NP values, [Bsz][K][L][NP] each
   int Bsz, Dm, L, H, W;
+  int N;                    // state size (the row kernel may run a larger power-of-two instantiation)
   int K, Ku;
   int kinds;                // 4 x 2-bit traversal kind, direction k at bits 2k..2k+1
   int nchunks;              // chunks per sequence (>= 1)
@@ -476,34 +478,40 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
 }
 
 // out[b][t][d] = (Σ_k ws_y[k][b][t][d]) · silu(z[b][t][d]), directions added in
-// ascending k; one thread per 8 consecutive channels.
-template <typename TIn>
+// ascending k; one thread per V consecutive elements (V = 8 when the channel
+// count is a multiple of 8, else 1).
+template <typename TIn, int V>
 __global__ void __launch_bounds__(256) merge_dirs_kernel(const float* __restrict__ ws_y, const TIn* __restrict__ z,
-                                                         TIn* __restrict__ out, int K, int64_t nrows8,
+                                                         TIn* __restrict__ out, int K, int64_t nvec,
                                                          int64_t plane) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= nrows8) return;
-  const int64_t off = i * 8;
-  float y8[8];
-  {
+  if (i >= nvec) return;
+  const int64_t off = i * V;
+  float y8[V];
+  if constexpr (V == 8) {
     const float4 a = reinterpret_cast<const float4*>(ws_y + off)[0];
     const float4 bq = reinterpret_cast<const float4*>(ws_y + off)[1];
     y8[0] = a.x; y8[1] = a.y; y8[2] = a.z; y8[3] = a.w;
     y8[4] = bq.x; y8[5] = bq.y; y8[6] = bq.z; y8[7] = bq.w;
-  }
-  for (int k = 1; k < K; ++k) {
-    const float4 a = reinterpret_cast<const float4*>(ws_y + k * plane + off)[0];
-    const float4 bq = reinterpret_cast<const float4*>(ws_y + k * plane + off)[1];
-    y8[0] += a.x; y8[1] += a.y; y8[2] += a.z; y8[3] += a.w;
-    y8[4] += bq.x; y8[5] += bq.y; y8[6] += bq.z; y8[7] += bq.w;
-  }
-  if (z) {
-    Vec<TIn, 8> zz;
-    zz.load(z + off);
+    for (int k = 1; k < K; ++k) {
+      const float4 a2 = reinterpret_cast<const float4*>(ws_y + k * plane + off)[0];
+      const float4 b2 = reinterpret_cast<const float4*>(ws_y + k * plane + off)[1];
+      y8[0] += a2.x; y8[1] += a2.y; y8[2] += a2.z; y8[3] += a2.w;
+      y8[4] += b2.x; y8[5] += b2.y; y8[6] += b2.z; y8[7] += b2.w;
+    }
+    if (z) {
+      Vec<TIn, 8> zz;
+      zz.load(z + off);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y8[j] *= silu_f(zz.get(j));
+      for (int j = 0; j < 8; ++j) y8[j] *= silu_f(zz.get(j));
+    }
+    storeV<8>(out + off, y8);
+  } else {
+    y8[0] = ws_y[off];
+    for (int k = 1; k < K; ++k) y8[0] += ws_y[k * plane + off];
+    if (z) y8[0] *= silu_f(load1(z + off));
+    store1(out + off, y8[0]);
   }
-  storeV<8>(out + off, y8);
 }
 
 // One recurrent step [MFS §2.3]: one thread per (b, d) holding all N states.
@@ -568,6 +576,37 @@ __global__ void __launch_bounds__(256) scan_step_kernel(const StepParams p) {
 #pragma unroll
   for (int m = 1; m < TPC; m <<= 1) y += __shfl_xor(y, m, TPC);
   if (n0 != 0) return;
+  y += (p.D ? p.D[d] : 0.f) * uu;
+  if (p.z_t) y *= silu_f(load1(static_cast<const TIn*>(p.z_t) + i));
+  store1(static_cast<TIn*>(p.out) + i, y);
+}
+
+// One token for any state size (those that are not a power of two): one
+// thread per (batch, channel) walking its N states.
+template <typename TIn, bool EXACT>
+__global__ void __launch_bounds__(256) scan_step_any_kernel(const StepParams p, int N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (b, d)
+  if (i >= (int64_t)p.Bsz * p.Dm) return;
+  const int b = (int)(i / p.Dm), d = (int)(i - (int64_t)b * p.Dm);
+  const float x = load1(static_cast<const TIn*>(p.delta_t) + i) + (p.delta_bias ? p.delta_bias[d] : 0.f);
+  const float dl = p.softplus ? softplus_log2(x) : x * kLog2e;  // Δ' = Δ·log2 e
+  const float uu = load1(static_cast<const TIn*>(p.u_t) + i);
+  const float du = dl * uu * kLn2;  // Δ·u
+  float* st = p.state + i * N;
+  const float* Ad = p.A + (int64_t)d * N;
+  const TIn* Bt = static_cast<const TIn*>(p.B_t) + (int64_t)b * N;
+  const TIn* Ct = static_cast<const TIn*>(p.C_t) + (int64_t)b * N;
+  float y = 0.f;
+  for (int n = 0; n < N; ++n) {
+    const float An = Ad[n];
+    const float a = ex2(dl * An);  // e^(Δ·A) = 2^(Δ'·A)
+    const float Bn = load1(Bt + n);
+    float bu = du * Bn;
+    if constexpr (EXACT) bu = zoh_coef(a, dl * An * kLn2, dl * kLn2, An != 0.f ? 1.0f / An : 0.f) * (uu * Bn);
+    const float hn = __builtin_fmaf(a, st[n], bu);
+    st[n] = hn;
+    y = __builtin_fmaf(load1(Ct + n), hn, y);
+  }
   y += (p.D ? p.D[d] : 0.f) * uu;
   if (p.z_t) y *= silu_f(load1(static_cast<const TIn*>(p.z_t) + i));
   store1(static_cast<TIn*>(p.out) + i, y);

@@ -10,6 +10,7 @@
 #include "../../include/mamba_scan.h"
 #include "scan_bwd.h"
 #include "scan_kernels.h"
+#include "scan_row.h"
 
 namespace mscan {
 
@@ -51,10 +52,15 @@ inline constexpr int threads_of(int N, int g16 = 1) { return layout_of(N, g16).c
 // (batch 32: 482 -> 497; the 130M layer at 3 waves per SIMD: 140 -> 180).
 inline constexpr int64_t kG2Waves = 16 * 1024;
 
+// Workspace of a forward pass, in this order (each region 256-byte aligned):
+// the per-direction fp32 rows, the time-split aggregates (end states, ΣΔ'),
+// and for the row kernel the fp32 copies of B and C.
 struct Plan {
   int K, Ku, cb, g, nblk_d, nchunks, chunk_len, prio;
-  size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes;
-  size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes; }
+  int row;  // 1: scan_row_kernel (one channel per lane, all states in registers); 0: scan_chunk_kernel
+  int np;   // the row kernel's power-of-two state count (>= N)
+  size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes, bc_bytes;
+  size_t total() const { return ws_y_bytes + agg_state_bytes + agg_dsum_bytes + bc_bytes; }
 };
 
 
@@ -63,12 +69,32 @@ struct Plan {
 // zero-order hold or Δ·B·u).
 #define MSCAN_DECLARE_DISPATCH(SUFFIX)                                                        \
   int dispatch_scan_##SUFFIX(int64_t N, const ScanParams& p, const Plan& pl, hipStream_t s); \
+  int dispatch_rows_##SUFFIX(const ScanParams& p, const Plan& pl, hipStream_t s);           \
   int dispatch_step_##SUFFIX(int64_t N, const StepParams& p, hipStream_t s);              \
   int dispatch_bwd_##SUFFIX(int64_t N, const BwdParams& p, hipStream_t s);
 MSCAN_DECLARE_DISPATCH(bf16_simple)
 MSCAN_DECLARE_DISPATCH(bf16_exact)
 MSCAN_DECLARE_DISPATCH(f32_simple)
 MSCAN_DECLARE_DISPATCH(f32_exact)
+
+#if defined(MSCAN_INSTANTIATE) || defined(MSCAN_INSTANTIATE_ROWS)
+template <typename TIn>
+int launch_merge(const ScanParams& p, hipStream_t stream) {
+  const int64_t n = (int64_t)p.Bsz * p.L * p.Dm;
+  if (p.Dm % 8 == 0) {
+    const int64_t rows8 = n / 8;
+    const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
+    hipLaunchKernelGGL((merge_dirs_kernel<TIn, 8>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
+                       static_cast<const TIn*>(p.z), static_cast<TIn*>(p.out), p.K, rows8, n);
+  } else {
+    const unsigned mblocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL((merge_dirs_kernel<TIn, 1>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
+                       static_cast<const TIn*>(p.z), static_cast<TIn*>(p.out), p.K, n, n);
+  }
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+#endif
 
 #ifdef MSCAN_INSTANTIATE
 template <typename TIn, int N, int G16, bool EXACT>
@@ -98,14 +124,7 @@ int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
     rc = launch_chunks<TIn, N, 1, EXACT>(p, pl, stream);
   }
   if (rc != MAMBA_OK) return rc;
-  if (p.ws_y && p.out && p.K > 1) {  // (with one direction the scan wrote out itself)
-    const int64_t rows8 = (int64_t)p.Bsz * p.L * p.Dm / 8;
-    const unsigned mblocks = (unsigned)((rows8 + 255) / 256);
-    hipLaunchKernelGGL((merge_dirs_kernel<TIn>), dim3(mblocks), dim3(256), 0, stream, p.ws_y,
-                       static_cast<const TIn*>(p.z), static_cast<TIn*>(p.out), p.K, rows8,
-                       (int64_t)p.Bsz * p.L * p.Dm);
-    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
-  }
+  if (p.ws_y && p.out && p.K > 1) return launch_merge<TIn>(p, stream);  // (K = 1: the scan wrote out)
   return MAMBA_OK;
 }
 
@@ -133,6 +152,11 @@ int launch_step(const StepParams& p, hipStream_t stream) {
 
 template <typename TIn, bool EXACT>
 int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
+  if ((N & (N - 1)) != 0) {
+    const unsigned blocks = (unsigned)(((int64_t)p.Bsz * p.Dm + 255) / 256);
+    hipLaunchKernelGGL((scan_step_any_kernel<TIn, EXACT>), dim3(blocks), dim3(256), 0, s, p, (int)N);
+    return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+  }
   switch (N) {
     case 1: return launch_step<TIn, 1, EXACT>(p, s);
     case 2: return launch_step<TIn, 2, EXACT>(p, s);
@@ -175,5 +199,64 @@ int dispatch_bwd(int64_t N, const BwdParams& p, hipStream_t s) {
 }
 
 #endif  // MSCAN_INSTANTIATE
+
+
+#ifdef MSCAN_INSTANTIATE_ROWS
+template <typename TIn, int NP, bool FULL, bool EXACT>
+int launch_rows(ScanParams p, const Plan& pl, hipStream_t stream) {
+  {
+    const int64_t rows = (int64_t)p.Bsz * p.K * p.L;
+    const unsigned wblocks = (unsigned)((2 * (rows + 2) * NP + 255) / 256);
+    int lognp = 0;
+    while ((1 << lognp) < NP) ++lognp;
+    hipLaunchKernelGGL((widen_bc_kernel<TIn>), dim3(wblocks), dim3(256), 0, stream, static_cast<const TIn*>(p.B),
+                       static_cast<const TIn*>(p.C), p.bcw, rows, p.N, lognp);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  if (pl.nchunks > 1) {
+    p.grid_chunks = pl.nchunks - 1;
+    const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
+    hipLaunchKernelGGL((scan_row_kernel<TIn, NP, FULL, ROW_AGG, EXACT>), dim3(blocks), dim3(64), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  p.grid_chunks = pl.nchunks;
+  const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
+  if (p.ckpt || (p.K == 1 && p.ws_y) || (p.K == 1 && !p.out) || (p.K != 1 && !p.ws_y))
+    hipLaunchKernelGGL((scan_row_kernel<TIn, NP, FULL, ROW_ANY, EXACT>), dim3(blocks), dim3(64), 0, stream, p);
+  else if (p.K != 1)
+    hipLaunchKernelGGL((scan_row_kernel<TIn, NP, FULL, ROW_ROWS, EXACT>), dim3(blocks), dim3(64), 0, stream, p);
+  else if (p.z)
+    hipLaunchKernelGGL((scan_row_kernel<TIn, NP, FULL, ROW_OUT_GATE, EXACT>), dim3(blocks), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((scan_row_kernel<TIn, NP, FULL, ROW_OUT, EXACT>), dim3(blocks), dim3(64), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+template <typename TIn, int NP, bool EXACT>
+int launch_scan_rows(const ScanParams& p, const Plan& pl, hipStream_t stream) {
+  // (state sizes up to 2 are powers of two: no padded instantiation)
+  int rc;
+  if constexpr (NP <= 2) rc = launch_rows<TIn, NP, true, EXACT>(p, pl, stream);
+  else rc = p.N == NP ? launch_rows<TIn, NP, true, EXACT>(p, pl, stream)
+                      : launch_rows<TIn, NP, false, EXACT>(p, pl, stream);
+  if (rc != MAMBA_OK) return rc;
+  if (p.ws_y && p.out && p.K > 1) return launch_merge<TIn>(p, stream);
+  return MAMBA_OK;
+}
+
+template <typename TIn, bool EXACT>
+int dispatch_rows(const ScanParams& p, const Plan& pl, hipStream_t s) {
+  switch (pl.np) {
+    case 1: return launch_scan_rows<TIn, 1, EXACT>(p, pl, s);
+    case 2: return launch_scan_rows<TIn, 2, EXACT>(p, pl, s);
+    case 4: return launch_scan_rows<TIn, 4, EXACT>(p, pl, s);
+    case 8: return launch_scan_rows<TIn, 8, EXACT>(p, pl, s);
+    case 16: return launch_scan_rows<TIn, 16, EXACT>(p, pl, s);
+    case 32: return launch_scan_rows<TIn, 32, EXACT>(p, pl, s);
+    case 64: return launch_scan_rows<TIn, 64, EXACT>(p, pl, s);
+    default: return MAMBA_ERR_UNSUPPORTED;
+  }
+}
+#endif  // MSCAN_INSTANTIATE_ROWS
 
 }  // namespace mscan

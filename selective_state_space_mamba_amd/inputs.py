@@ -137,3 +137,61 @@ def make_dout(w: Workload, seqlen: int | None = None) -> np.ndarray:
     L = w.seqlen if seqlen is None else seqlen
     rng = np.random.Generator(np.random.PCG64([w.seed, 2]))
     return _normal(rng, (w.batch, L, w.dim), w.dtype)
+
+
+def make_inputs_device(w: Workload, device, seed: int | None = None) -> dict:
+    """The make_inputs recipe drawn on a GPU with torch's generator, for the
+    throughput measurement of workloads too large to draw quickly on the host:
+    the same shapes and distributions (A = -(n + 1); dt log-uniform in
+    [1e-3, 1e-1] and delta_bias = log(expm1(dt)); u, delta, z, B, C, D standard
+    normal, rounded to bfloat16 to nearest even for the bf16 workloads), not the
+    same values as make_inputs.  Returns torch tensors on `device`."""
+    import torch
+    K, Bsz, L, Dm, N = w.ndirs, w.batch, w.seqlen, w.dim, w.dstate
+    Ku = 1 if w.dir_mode == DIR_CROSS2D else K
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed if seed is None else seed)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def normal(shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(tdt)
+
+    A = -(torch.arange(N, device=device, dtype=torch.float32) + 1.0).expand(K, Dm, N).contiguous()
+    lo, hi = float(np.log(1e-3)), float(np.log(1e-1))
+    dt = torch.exp(torch.rand((K, Dm), generator=g, device=device, dtype=torch.float64) * (hi - lo) + lo)
+    delta_bias = torch.log(torch.expm1(dt)).to(torch.float32)
+    ushape = (Bsz, L, Dm) if Ku == 1 else (Bsz, Ku, L, Dm)
+    dshape = (Bsz, L, Dm) if K == 1 else (Bsz, K, L, Dm)
+    bshape = (Bsz, L, N) if K == 1 else (Bsz, K, L, N)
+    x = dict(u=normal(ushape), delta=normal(dshape), z=normal((Bsz, L, Dm)) if w.gated else None,
+             B=normal(bshape), C=normal(bshape), A=A,
+             D=torch.randn((K, Dm), generator=g, device=device, dtype=torch.float32), delta_bias=delta_bias)
+    if K == 1:
+        x["A"], x["D"], x["delta_bias"] = x["A"].reshape(Dm, N), x["D"].reshape(Dm), x["delta_bias"].reshape(Dm)
+    return x
+
+
+def host_channel_sample(w: Workload, xd: dict, channels) -> dict:
+    """The inputs of a subset of channels (all batches, directions, tokens and
+    states), copied from device tensors made by make_inputs_device to numpy
+    arrays in the layout make_inputs returns (bf16 as uint16 bit patterns).
+    Channels are independent rows of the scan, so the subset is a workload of
+    its own with dim = len(channels)."""
+    import torch
+    idx = torch.as_tensor(np.asarray(channels, dtype=np.int64), device=xd["u"].device)
+
+    def host(t, last_is_channel=True):
+        if t is None:
+            return None
+        if last_is_channel:
+            t = t.index_select(t.dim() - 1, idx)
+        t = t.contiguous().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    out = {k: host(xd[k]) for k in ("u", "delta", "z", "D", "delta_bias")}
+    out["A"] = host(xd["A"].index_select(xd["A"].dim() - 2, idx), last_is_channel=False)
+    out["B"] = host(xd["B"], last_is_channel=False)
+    out["C"] = host(xd["C"], last_is_channel=False)
+    return out

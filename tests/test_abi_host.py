@@ -89,7 +89,13 @@ def test_fwd_validation(lib):
     assert call_fwd(lib, dims(), mode=9) == ms._binding.MAMBA_ERR_INVALID
     assert call_fwd(lib, dims(seqlen=96, height=8, width=11), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
     assert call_fwd(lib, dims(seqlen=96), mode=ms.DIR_CROSS2D) == ms._binding.MAMBA_ERR_INVALID
-    assert call_fwd(lib, dims(dstate=12)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    # any state size 1..64 and (float32) any channel count that is a multiple of 4
+    for n in (1, 3, 12, 24, 48, 63, 64):
+        assert ms.workspace_bytes(dims(dstate=n), ms.DIR_FWD) >= 0
+    assert ms.workspace_bytes(dims(dim=36, dtype=ms.DTYPE_F32), ms.DIR_FWD) >= 0
+    assert call_fwd(lib, dims(dstate=65)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(dim=34, dtype=ms.DTYPE_F32)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert call_fwd(lib, dims(dim=36, dtype=ms.DTYPE_BF16)) == ms._binding.MAMBA_ERR_UNSUPPORTED
     # 32-bit slice offsets: (seqlen + 64) * dim * sizeof(dtype) must stay below 2^31 bytes
     dim = 1 << 16
     lmax = (2**31 - 1) // (dim * 2) - 64
@@ -118,7 +124,8 @@ def test_step_validation(lib):
                                    ctypes.byref(d), p["out"], None)
     assert step(dims(), state=None) == ms._binding.MAMBA_ERR_INVALID
     assert step(dims(dim=0)) == ms._binding.MAMBA_ERR_INVALID
-    assert step(dims(dstate=3)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert step(dims(dstate=65)) == ms._binding.MAMBA_ERR_UNSUPPORTED
+    assert step(dims(dim=36)) == ms._binding.MAMBA_ERR_UNSUPPORTED  # bf16: a multiple of 8
     assert step(dims(), B=FAKE + 8) == ms._binding.MAMBA_ERR_UNSUPPORTED
     assert lib.mamba_scan_step(None, None, None, None, None, None, None, None, None, None, None, None) == \
         ms._binding.MAMBA_ERR_INVALID
@@ -149,7 +156,7 @@ def test_bwd_workspace_and_validation(lib):
     assert need % 256 == 0 and ms.bwd_workspace_bytes(d, ms.DIR_FWD) == need
     cross = ms.bwd_workspace_bytes(dims(seqlen=96, height=8, width=12), ms.DIR_CROSS2D)
     assert cross >= 4 * 4 * Bz * 96 * Dm * 2  # per-direction rows and per-direction du
-    for bad in (dims(dstate=32), dims(dstate=64), dims(seqlen=0), dims(dim=60)):
+    for bad in (dims(dstate=32), dims(dstate=64), dims(dstate=12), dims(seqlen=0), dims(dim=60)):
         with pytest.raises(ms.MambaError):
             ms.bwd_workspace_bytes(bad, ms.DIR_FWD)
 

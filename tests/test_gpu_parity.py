@@ -109,6 +109,30 @@ def test_state_size_64_bidir():
     run_and_check(I.Workload("N64_bidir", 1, 64, 50, 64, I.DIR_BIDIR, "f32", True, 131))
 
 
+# state sizes that are not a power of two (run padded to the next one, the
+# extra states held at zero) and float32 channel counts that are a multiple
+# of 4 but not of 8
+ODD = {
+    "N3_fwd_f32": I.Workload("N3_fwd_f32", 2, 80, 70, 3, I.DIR_FWD, "f32", True, 141),
+    "N3_fwd_bf16": I.Workload("N3_fwd_bf16", 2, 80, 71, 3, I.DIR_FWD, "bf16", True, 142),
+    "N12_fwd_bf16": I.Workload("N12_fwd_bf16", 2, 136, 97, 12, I.DIR_FWD, "bf16", True, 143),
+    "N12_bidir_f32": I.Workload("N12_bidir_f32", 2, 72, 65, 12, I.DIR_BIDIR, "f32", True, 144),
+    "N24_cross2d_bf16": I.Workload("N24_cross2d_bf16", 1, 64, 63, 24, I.DIR_CROSS2D, "bf16", False, 145, 7, 9),
+    "N48_fwd_f32": I.Workload("N48_fwd_f32", 1, 72, 90, 48, I.DIR_FWD, "f32", True, 146),
+    "N48_bwd_bf16": I.Workload("N48_bwd_bf16", 2, 64, 50, 48, I.DIR_BWD, "bf16", True, 147),
+    "N12_split_bf16": I.Workload("N12_split_bf16", 1, 64, 5000, 12, I.DIR_FWD, "bf16", True, 148),
+    "D36_fwd_f32": I.Workload("D36_fwd_f32", 2, 36, 77, 16, I.DIR_FWD, "f32", True, 149),
+    "D36_bidir_f32": I.Workload("D36_bidir_f32", 2, 36, 45, 16, I.DIR_BIDIR, "f32", True, 150),
+    "D36_cross2d_f32_N5": I.Workload("D36_cross2d_f32_N5", 1, 36, 30, 5, I.DIR_CROSS2D, "f32", True, 151, 5, 6),
+    "D100_split_f32_N24": I.Workload("D100_split_f32_N24", 1, 100, 4100, 24, I.DIR_FWD, "f32", True, 152),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ODD))
+def test_odd_state_sizes_and_channel_counts(name):
+    run_and_check(ODD[name])
+
+
 def test_options_softplus_off_no_skip_no_gate_no_bias():
     w = I.Workload("opts", 2, 64, 90, 16, I.DIR_FWD, "f32", False, 31)
     x = I.make_inputs(w)
@@ -322,6 +346,14 @@ def test_decode_state_sizes(N):
     assert_close("decode N=%d state" % N, st, ref_st[:, 0], "f32")
 
 
+@pytest.mark.parametrize("N,dtype,dim", [(3, "f32", 40), (12, "bf16", 72), (24, "f32", 36), (48, "bf16", 64)])
+def test_decode_odd_state_sizes(N, dtype, dim):
+    w = I.Workload("dec_N%d" % N, 2, dim, 0, N, I.DIR_FWD, dtype, True, 60 + N)
+    got, st, ref_out, ref_st = run_decode(w, 45, 10)
+    assert_close("decode N=%d out" % N, got, ref_out[:, 45:], dtype)
+    assert_close("decode N=%d state" % N, st, ref_st[:, 0], dtype)
+
+
 def test_decode_exact_zoh():
     w = I.Workload("dec_exact", 2, 64, 0, 16, I.DIR_FWD, "f32", True, 53)
     got, st, ref_out, ref_st = run_decode(w, 80, 24, exact_zoh=True)
@@ -388,40 +420,65 @@ def test_exact_zoh_is_the_gated_rnn():
 # ---------------------------------------------------------------------------------------------
 # the specified workloads at full size, sampled rows
 
-def full_size_check(w, nrows=48, seed=7, exact_zoh=False):
+def block_rows(rng, batch, dim, block=16):
+    """For every batch and every block of `block` channels: both edge
+    channels and one channel drawn inside the block."""
+    rows = set()
+    for b in range(batch):
+        for d0 in range(0, dim, block):
+            d1 = min(dim, d0 + block) - 1
+            rows.update({(b, d0), (b, d1), (b, int(rng.integers(d0, d1 + 1)))})
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def full_size_check(w, rows="all", seed=7, exact_zoh=False):
+    """The whole output and last state against the oracle (rows="all"), or the
+    (b, d) rows of an int array [R, 2]."""
     x = I.make_inputs(w)
-    announce("full-size %s exact_zoh=%s" % (w.name, exact_zoh))
+    announce("full-size %s exact_zoh=%s rows=%s" % (w.name, exact_zoh, "all" if isinstance(rows, str) else len(rows)))
     out, st = gpu_fwd(w, dev_inputs(x), exact_zoh=exact_zoh)
-    rows = sample_rows(np.random.Generator(np.random.PCG64(seed)), w.batch, w.dim, nrows)
-    ref_out, ref_st = oracle_fwd(w, x, rows=rows, exact_zoh=exact_zoh)
     o = from_dev(out)
     s = from_dev(st).reshape(w.batch, w.ndirs, w.dim, w.dstate)
+    if isinstance(rows, str):
+        ref_out, ref_st = oracle_fwd(w, x, exact_zoh=exact_zoh)
+        assert_close(w.name + " out (every row)", o, ref_out, w.dtype)
+        assert_close(w.name + " last_state (every row)", s, ref_st.reshape(s.shape), w.dtype)
+        return
+    ref_out, ref_st = oracle_fwd(w, x, rows=rows, exact_zoh=exact_zoh)
     got_o = np.stack([o[b, :, d] for b, d in rows])
     got_s = np.stack([s[b, :, d] for b, d in rows])
-    assert_close(w.name + " out (sampled rows)", got_o, ref_out, w.dtype)
-    assert_close(w.name + " last_state (sampled rows)", got_s, ref_st, w.dtype)
+    assert_close(w.name + " out (%d rows)" % len(rows), got_o, ref_out, w.dtype)
+    assert_close(w.name + " last_state (%d rows)" % len(rows), got_s, ref_st, w.dtype)
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["mamba130m_layer", "long_context", "vim_bidir_224", "vim_bidir_1248",
-                                  "vmamba_ss2d"])
-def test_full_size_workloads(name):
+@pytest.mark.parametrize("name", ["mamba130m_layer", "vim_bidir_224", "vmamba_ss2d"])
+def test_full_size_workloads_every_row(name):
     full_size_check(I.WORKLOADS[name])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["long_context", "vim_bidir_1248"])
+def test_full_size_long_workloads(name):
+    """Few rows, long sequences: three channels of every 16-channel block (the
+    two edges and one inside), every token of each."""
+    w = I.WORKLOADS[name]
+    full_size_check(w, rows=block_rows(np.random.Generator(np.random.PCG64(7)), w.batch, w.dim))
 
 
 @pytest.mark.parametrize("name", ["mamba130m_layer", "vim_bidir_224"])
 def test_full_size_exact_zoh(name):
     """The exact input-term rule in the launch configuration the benchmark
     times for it, sampled rows against the oracle."""
-    full_size_check(I.WORKLOADS[name], exact_zoh=True)
+    w = I.WORKLOADS[name]
+    full_size_check(w, rows=sample_rows(np.random.Generator(np.random.PCG64(7)), w.batch, w.dim, 48),
+                    exact_zoh=True)
 
 
 @pytest.mark.slow
 def test_full_size_decode_512_steps():
+    """512 decode steps continuing the full 2048-token scan, every row."""
     w = I.WORKLOADS["mamba130m_layer"]
-    rows = sample_rows(np.random.Generator(np.random.PCG64(8)), w.batch, w.dim, 32)
-    got, st, ref_out, ref_st = run_decode(w, w.seqlen, I.DECODE_STEPS, rows=rows)
-    got_rows = np.stack([got[b, :, d] for b, d in rows])
-    st_rows = np.stack([st[b, d] for b, d in rows])
-    assert_close("decode512 out (sampled rows)", got_rows, ref_out[:, w.seqlen:], "bf16")
-    assert_close("decode512 state (sampled rows)", st_rows, ref_st[:, 0], "bf16")
+    got, st, ref_out, ref_st = run_decode(w, w.seqlen, I.DECODE_STEPS)
+    assert_close("decode512 out (every row)", got, ref_out[:, w.seqlen:], "bf16")
+    assert_close("decode512 state (every row)", st, ref_st[:, 0], "bf16")
