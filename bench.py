@@ -409,6 +409,16 @@ def main():
                 ms.scan_step(st, ut, dt_, s0["A"], Bt, Ct, s0["D"], zt, s0["delta_bias"], out=o, stream=stream)
             torch.cuda.synchronize()
             dec_s = time.perf_counter() - t0
+            # the same loop through a ScanStepper (fixed operands checked once)
+            stepper = ms.ScanStepper(st, s0["A"], s0["D"], s0["delta_bias"], dtype=ut.dtype, stream=stream)
+            for _ in range(10):
+                stepper(ut, dt_, Bt, Ct, zt, out=o)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.decode_steps):
+                stepper(ut, dt_, Bt, Ct, zt, out=o)
+            torch.cuda.synchronize()
+            sdec_s = time.perf_counter() - t0
         # the same loop captured once as a HIP graph and replayed (no host
         # work per step): the kernel-bound rate of the decode loop
         graph = torch.cuda.CUDAGraph()
@@ -427,6 +437,7 @@ def main():
         gdec_s = time.perf_counter() - t0
         del graph
         decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
+                  "stepper_us_per_step": sdec_s * 1e6 / args.decode_steps,
                   "graph_us_per_step": gdec_s * 1e6 / args.decode_steps,
                   "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4,
                   "elements_per_step": w.batch * w.dim * w.dstate,

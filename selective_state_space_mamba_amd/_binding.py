@@ -163,6 +163,8 @@ def saved_bytes(dims: MambaDims, dir_mode: int, gated: bool) -> int:
 def _check(t, name, shape, dtype, device):
     if t is None:
         return
+    if t.shape == shape and t.dtype == dtype and t.is_contiguous() and t.device == device:
+        return  # (the common case, without building messages)
     if tuple(t.shape) != tuple(shape):
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if t.dtype != dtype:
@@ -402,6 +404,60 @@ def scan_step(state, u_t, delta_t, A, B_t, C_t, D=None, z_t=None, delta_bias=Non
     if rc != MAMBA_OK:
         raise MambaError(rc, "mamba_scan_step")
     return out
+
+
+class ScanStepper:
+    """Repeated mamba_scan_step calls of a decode loop [MFS §2.3]: the state,
+    A, D and delta_bias, the options and the launch stream are checked and
+    marshalled once here; each call then checks only its own [B][D] and
+    [B][N] tensors (shape, dtype, contiguity, device) and makes one C call.
+    state is updated in place on every call, as by scan_step.  stream: the
+    launch stream (torch stream or raw handle), fixed at construction; None
+    takes torch's current stream at construction time."""
+
+    def __init__(self, state, A, D=None, delta_bias=None, *, dtype, delta_softplus=True, exact_zoh=False,
+                 stream=None):
+        import torch
+        self._lib = load_library()
+        dev = state.device
+        if state.dim() != 3:
+            raise ValueError("state must be [B][D][N], got %s" % (tuple(state.shape),))
+        Bsz, Dm, N = state.shape
+        dt = _dtype_code(torch.empty(0, dtype=dtype))
+        _check(state, "state", (Bsz, Dm, N), torch.float32, dev)
+        _check(A, "A", (Dm, N), torch.float32, dev)
+        _check(D, "D", (Dm,), torch.float32, dev)
+        _check(delta_bias, "delta_bias", (Dm,), torch.float32, dev)
+        self._keep = (state, A, D, delta_bias)  # the pointers below stay valid while these live
+        self._dims = make_dims(Bsz, Dm, 1, N, dt, delta_softplus=delta_softplus, exact_zoh=exact_zoh)
+        self._dims_ref = ctypes.byref(self._dims)
+        self._state, self._A, self._D, self._bias = _ptr(state), _ptr(A), _ptr(D), _ptr(delta_bias)
+        self._stream = _stream(stream)
+        self._bd = torch.Size((Bsz, Dm))
+        self._bn = torch.Size((Bsz, N))
+        self._dtype = dtype
+        self._device = dev
+
+    def _ok(self, t, name, shape):
+        if not (t.shape == shape and t.dtype == self._dtype and t.is_contiguous() and t.device == self._device):
+            _check(t, name, shape, self._dtype, self._device)  # raises with the reason
+
+    def __call__(self, u_t, delta_t, B_t, C_t, z_t=None, *, out):
+        """One step: u_t, delta_t, z_t, out [B][D]; B_t, C_t [B][N]."""
+        bd, bn = self._bd, self._bn
+        self._ok(u_t, "u_t", bd)
+        self._ok(delta_t, "delta_t", bd)
+        self._ok(B_t, "B_t", bn)
+        self._ok(C_t, "C_t", bn)
+        if z_t is not None:
+            self._ok(z_t, "z_t", bd)
+        self._ok(out, "out", bd)
+        rc = self._lib.mamba_scan_step(self._state, u_t.data_ptr(), delta_t.data_ptr(), self._A, B_t.data_ptr(),
+                                       C_t.data_ptr(), self._D, None if z_t is None else z_t.data_ptr(),
+                                       self._bias, self._dims_ref, out.data_ptr(), self._stream)
+        if rc != MAMBA_OK:
+            raise MambaError(rc, "mamba_scan_step")
+        return out
 
 
 def conv1d_silu(x, weight, bias=None, *, reverse=False, out=None, stream=None):

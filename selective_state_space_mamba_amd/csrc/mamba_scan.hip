@@ -414,6 +414,7 @@ int run_fwd(const void* u, const void* delta, const float* A, const void* B, con
   p.out = out;
   set_workspace(&p, pl, ws, true, ws + pl.ws_y_bytes);
   p.last_state = last_state;
+  p.fold = 1;  // the per-direction rows are not kept: the last direction may sum them
   return dispatch_fwd(dims, p, pl, stream);
 }
 

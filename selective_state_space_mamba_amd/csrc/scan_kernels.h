@@ -40,6 +40,14 @@
 
 namespace mscan {
 
+// Quads (4 scan steps) ahead at which the scan loop reads its LDS operands:
+// 2 with one state per thread in 16-channel blocks (the 130M layer: 147.0 ->
+// 143.6 µs on MI355X), 1 otherwise (2 states per thread have no registers to
+// spare: Vim-224 234 -> 286 µs).
+#ifndef MSCAN_LDS_PD
+#define MSCAN_LDS_PD 0  // 0: the choice above; 1, 2, 3: that depth everywhere
+#endif
+
 // Traversal kinds: token index of scan position p.
 enum : int { KIND_ROW_FWD = 0, KIND_ROW_REV = 1, KIND_COL_FWD = 2, KIND_COL_REV = 3 };
 
@@ -80,6 +88,10 @@ struct ScanParams {
   int softplus;
   int ckpt_tiles;           // tiles of TT positions per sequence (checkpoint rows)
   int prio;                 // 1: the scan loop runs at raised wave priority (16-channel blocks)
+  int kbase;                // first direction of this launch's grid
+  int fold;                 // 1: the launch's direction (the last, k = K-1) adds the rows of
+                            // directions 0..K-2 from ws_y, in ascending k, to its own output
+                            // and writes the gated result to out (no merge kernel, no row of its own)
 };
 // Template flag EXACT of the kernels below: exact zero-order-hold input term
 // ((e^{ΔA} - 1)/A)·B·u instead of Δ·B·u [MFS §6.2 Step 4, eq (4)].
@@ -156,7 +168,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   const int c = bid % p.grid_chunks;
   bid /= p.grid_chunks;
   const int b = bid % p.Bsz;
-  const int k = bid / p.Bsz;
+  const int k = p.kbase + bid / p.Bsz;
 
   const int D = p.Dm, L = p.L;
   const int d0 = dblk * CB;
@@ -177,9 +189,11 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   const auto rs_u = make_rsrc(u_slice, slice);
   const auto rs_dl = make_rsrc(dl_slice, slice);
   const auto rs_z = make_rsrc(p.z ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : nullptr, p.z ? slice : 0u);
-  // the gated output row is written here only with one direction; the
-  // ungated fp32 rows whenever ws_y is given
-  const bool direct = !AGG && p.out != nullptr && p.K == 1;
+  // the gated output row is written here with one direction, or by the
+  // folding last direction; the ungated fp32 rows whenever ws_y is given
+  // (except by the folding direction, which reads them)
+  const bool fold = !AGG && p.fold != 0;
+  const bool direct = !AGG && p.out != nullptr && (p.K == 1 || fold);
   const auto rs_ws = make_rsrc(p.ws_y ? p.ws_y + ((int64_t)k * p.Bsz + b) * L * D : nullptr,
                                p.ws_y ? (uint32_t)((int64_t)L * D * 4) : 0u);
   const auto rs_out = make_rsrc(direct ? static_cast<TIn*>(p.out) + (int64_t)b * L * D : nullptr, direct ? slice : 0u);
@@ -232,12 +246,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     Small<TIn, EQ> B[BCI], C[BCI];
   };
   Raw r0, r1;
-  float Du[TPT], gate[TPT];
+  float Du[TPT], gate[TPT], folded[TPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     r0.dl[i] = r0.u[i] = r0.z[i] = r1.dl[i] = r1.u[i] = r1.z[i] = TIn(0);
     Du[i] = 0.f;
     gate[i] = 1.f;
+    folded[i] = 0.f;
   }
 #pragma unroll
   for (int i = 0; i < BCI; ++i) {
@@ -300,6 +315,23 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       if constexpr (!AGG) {
         Du[i] = Dd * uu;
         if (gated) gate[i] = silu_f(to_f32(r.z[i]));
+      }
+    }
+    if constexpr (!AGG) {
+      if (fold) {
+        // the earlier directions' rows at this thread's epilogue positions,
+        // summed in ascending k (read here, a whole tile before their use)
+#pragma unroll
+        for (int i = 0; i < TPT; ++i) {
+          const uint32_t roff = row_off(p0 + ng * TPT + i, 4u);
+          float acc = 0.f;
+          for (int kk = 0; kk < k; ++kk) {
+            const auto rs = make_rsrc(p.ws_y + ((int64_t)kk * p.Bsz + b) * L * D, (uint32_t)((int64_t)L * D * 4));
+            const float v = buf_load(rs, CB == 64 ? voff_ws : voff_ws + roff, CB == 64 ? roff : 0u, (float*)nullptr);
+            acc = kk == 0 ? v : acc + v;
+          }
+          folded[i] = acc;
+        }
       }
     }
 #pragma unroll
@@ -404,16 +436,32 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       }
     };
     if (CB == 64 || p.prio) __builtin_amdgcn_s_setprio(1);
-    Ops o0, o1;
-    read_ops(o0, 0);
+    constexpr int PDQ = MSCAN_LDS_PD ? MSCAN_LDS_PD : (G == 1 && CB == 16 ? 2 : 1);
+    if constexpr (PDQ > 1) {
+      // operands read PDQ quads ahead, in a ring of register sets
+      constexpr int NQ = TT / 4;
+      Ops ring[PDQ + 1];
 #pragma unroll
-    for (int tt = 0; tt < TT; tt += 8) {
-      if (tt < tend) {
-        read_ops(o1, tt + 4);
-        quad(o0, tt);
-        if (tt + 4 < tend) {
-          read_ops(o0, min(tt + 8, TT - 4));  // the last prefetch re-reads rows that go unused
-          quad(o1, tt + 4);
+      for (int q = 0; q < PDQ && q < NQ; ++q) read_ops(ring[q], 4 * q);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        if (4 * q < tend) {
+          if (q + PDQ < NQ) read_ops(ring[(q + PDQ) % (PDQ + 1)], 4 * (q + PDQ));
+          quad(ring[q % (PDQ + 1)], 4 * q);
+        }
+      }
+    } else {
+      Ops o0, o1;
+      read_ops(o0, 0);
+#pragma unroll
+      for (int tt = 0; tt < TT; tt += 8) {
+        if (tt < tend) {
+          read_ops(o1, tt + 4);
+          quad(o0, tt);
+          if (tt + 4 < tend) {
+            read_ops(o0, min(tt + 8, TT - 4));  // the last prefetch re-reads rows that go unused
+            quad(o1, tt + 4);
+          }
         }
       }
     }
@@ -435,13 +483,14 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       for (int i = 0; i < TPT; ++i) {
         const int pp = p0 + ng * TPT + i;
         if (pp < pend && (dfull || dvalid)) {
-          if (p.ws_y) {
+          if (p.ws_y && !fold) {
             const uint32_t roff = row_off(pp, 4u);
             buf_store(yv[i], rs_ws, CB == 64 ? voff_ws : voff_ws + roff, CB == 64 ? roff : 0u);
           }
           if (direct) {
             const uint32_t roff = row_off(pp, ES);
-            store_out(gated ? yv[i] * gate[i] : yv[i], rs_out, CB == 64 ? voff_out : voff_out + roff,
+            const float yo = fold ? folded[i] + yv[i] : yv[i];
+            store_out(gated ? yo * gate[i] : yo, rs_out, CB == 64 ? voff_out : voff_out + roff,
                       CB == 64 ? roff : 0u, (TIn*)nullptr);
           }
         }

@@ -29,6 +29,9 @@ inline constexpr int kTile = MSCAN_TILE;  // scan positions per LDS tile
 #ifndef MSCAN_MIN_CHUNK
 #define MSCAN_MIN_CHUNK 1024     // shortest time chunk worth a separate aggregate pass
 #endif
+#ifndef MSCAN_FOLD
+#define MSCAN_FOLD 1
+#endif
 #ifndef MSCAN_MAX_CHUNKS
 #define MSCAN_MAX_CHUNKS 256
 #endif
@@ -97,6 +100,14 @@ int launch_merge(const ScanParams& p, hipStream_t stream) {
 #endif
 
 #ifdef MSCAN_INSTANTIATE
+// Whether the channel-block kernel's last direction folds the other
+// direction's row into the output (p.fold, set by the plain forward pass: the
+// rows are not kept) instead of a merge kernel summing the rows afterwards.
+// Two directions only -- measured on MI355X (fold vs merge, µs): 97k-token
+// Vim 1270 vs 1315, Vim-224 234 vs 236; the cross scan's fourth direction
+// alone fills a quarter of the GPU and loses: 999 vs 674.
+inline bool folds(const ScanParams& p) { return MSCAN_FOLD && p.fold && p.K == 2 && p.out && p.ws_y; }
+
 template <typename TIn, int N, int G16, bool EXACT>
 int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
   constexpr Layout lay = layout_of(N, G16);
@@ -109,10 +120,24 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.grid_chunks = pl.nchunks;
-  const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
   p.prio = pl.prio;
-  hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
-  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+  // directions kbase .. kbase+kcount-1 in one grid
+  auto run = [&](int kbase, int kcount, int fold) {
+    ScanParams q = p;
+    q.kbase = kbase;
+    q.fold = fold;
+    const unsigned blocks = (unsigned)(pl.nblk_d * q.grid_chunks * q.Bsz * kcount);
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0,
+                       stream, q);
+    return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+  };
+  if (folds(p)) {
+    // direction 0 writes its row, then direction 1 adds it to its own output
+    // in its epilogue
+    const int rc = run(0, p.K - 1, 0);
+    return rc != MAMBA_OK ? rc : run(p.K - 1, 1, 1);
+  }
+  return run(0, p.K, 0);
 }
 
 template <typename TIn, int N, bool EXACT>
@@ -124,7 +149,8 @@ int launch_scan(const ScanParams& p, const Plan& pl, hipStream_t stream) {
     rc = launch_chunks<TIn, N, 1, EXACT>(p, pl, stream);
   }
   if (rc != MAMBA_OK) return rc;
-  if (p.ws_y && p.out && p.K > 1) return launch_merge<TIn>(p, stream);  // (K = 1: the scan wrote out)
+  // (K = 1 or folded: the scan wrote out)
+  if (p.ws_y && p.out && p.K > 1 && !folds(p)) return launch_merge<TIn>(p, stream);
   return MAMBA_OK;
 }
 

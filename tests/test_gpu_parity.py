@@ -361,6 +361,35 @@ def test_decode_exact_zoh():
     assert_close("decode exact state", st, ref_st[:, 0], "f32")
 
 
+@pytest.mark.parametrize("N,dtype", [(16, "bf16"), (12, "f32")])
+def test_stepper_is_scan_step(N, dtype):
+    """ScanStepper runs the same kernel as scan_step: equal outputs and state,
+    bit for bit, over 24 steps from a scanned state; a mis-shaped tensor is
+    refused before any launch."""
+    t = torch()
+    w = I.Workload("stepper", 3, 40, 0, N, I.DIR_FWD, dtype, True, 54)
+    steps = 24
+    x = I.make_inputs(w, seqlen=32 + steps)
+    xd = dev_inputs({k: (np.ascontiguousarray(v[:, :32]) if k in ("u", "delta", "B", "C", "z") else v)
+                     for k, v in x.items()})
+    announce("stepper N=%d %s" % (N, dtype))
+    _, st = gpu_fwd(w.with_(seqlen=32), xd)
+    st_a = st.contiguous().clone()
+    st_b = st.contiguous().clone()
+    tail = {k: to_dev(np.ascontiguousarray(x[k][:, 32:].swapaxes(0, 1))) for k in ("u", "delta", "B", "C", "z")}
+    stepper = ms.ScanStepper(st_b, xd["A"], xd["D"], xd["delta_bias"], dtype=tail["u"].dtype)
+    for s in range(steps):
+        a = {k: tail[k][s].clone() for k in tail}
+        oa = ms.scan_step(st_a, a["u"], a["delta"], xd["A"], a["B"], a["C"], xd["D"], a["z"], xd["delta_bias"])
+        ob = stepper(a["u"], a["delta"], a["B"], a["C"], a["z"], out=t.empty_like(oa))
+        assert t.equal(oa, ob), s
+    t.cuda.synchronize()
+    assert t.equal(st_a, st_b)
+    bad = tail["B"][0][:, :N - 1].contiguous()
+    with pytest.raises(ValueError):
+        stepper(tail["u"][0], tail["delta"][0], bad, tail["C"][0], tail["z"][0], out=t.empty_like(tail["u"][0]))
+
+
 # ---------------------------------------------------------------------------------------------
 # exact zero-order hold of the input term
 
