@@ -83,9 +83,12 @@ def source_hash() -> str:
     h = hashlib.sha256()
     for f in ("include/mamba_scan.h", "selective_state_space_mamba_amd/csrc/mamba_scan.hip",
               "selective_state_space_mamba_amd/csrc/scan_inst.hip",
+              "selective_state_space_mamba_amd/csrc/row_inst.hip",
               "selective_state_space_mamba_amd/csrc/scan_launch.h",
               "selective_state_space_mamba_amd/csrc/scan_kernels.h",
-              "selective_state_space_mamba_amd/csrc/device_math.h"):
+              "selective_state_space_mamba_amd/csrc/scan_row.h",
+              "selective_state_space_mamba_amd/csrc/device_math.h",
+              "selective_state_space_mamba_amd/build.py"):
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
@@ -94,10 +97,11 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
+def measured_traffic(workload: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes from the committed rocprofv3 counter summary
     (profiles/scan_fwd_<workload>_counters.md), if it was taken on the current
-    kernel sources; else None."""
+    kernel sources; else None.  key: hbm_bytes_per_launch (the scan kernel's
+    output launch) or hbm_bytes_per_call (every kernel of one forward call)."""
     path = os.path.join(ROOT, "profiles", "scan_fwd_%s_counters.md" % workload)
     if not os.path.exists(path):
         return None
@@ -105,11 +109,11 @@ def measured_traffic(workload: str):
     with open(path) as fh:
         for line in fh:
             parts = line.strip().split(":", 1)
-            if len(parts) == 2 and parts[0] in ("source_hash", "hbm_bytes_per_launch"):
+            if len(parts) == 2 and parts[0] in ("source_hash", key):
                 rec[parts[0]] = parts[1].strip()
-    if rec.get("source_hash") != source_hash() or "hbm_bytes_per_launch" not in rec:
+    if rec.get("source_hash") != source_hash() or key not in rec:
         return None
-    return int(rec["hbm_bytes_per_launch"])
+    return int(rec[key])
 
 
 def cpu_baseline(w, x=None, budget_s: float = 15.0, sample_note: str = ""):
@@ -277,7 +281,8 @@ def time_config(torch, ms, I, w, steps: int, warm_ms: float, stream, cpu: bool):
            "min_us": float(np.min(launch_ms)) * 1e3, "elements": el, "elements_per_s": el / avg,
            "alu_frac": el / avg / ALU_PEAK_ELEM, "algorithmic_bytes": alg, "hbm_gbs": alg / avg / 1e9,
            "hbm_frac": alg / avg / 1e9 / HBM_PEAK_GBS, "workspace_bytes": int(ws.numel()),
-           "traffic": measured_traffic(w.name)}
+           "traffic": measured_traffic(w.name, "hbm_bytes_per_call"),
+           "traffic_unit": "HBM bytes per forward call, every kernel of it (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE)"}
     rec["copy_ceiling"] = copy_ceiling(torch, stream, alg)
     if cpu:
         # a channel sample: every batch, direction and token of 2 to 256 channels,

@@ -203,7 +203,7 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 // and per-batch partial sums of dA, dD and ddelta_bias, and the adjoint's
 // time-split carries.
 constexpr int kBwdBlock = 16;     // channels per workgroup of scan_bwd_kernel
-constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per CU)
+constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per CU; 1 at N = 32)
 constexpr int kBwdMinChunk = 1024;  // shortest time chunk of a split adjoint
 struct BwdPlan {
   Plan fwd;
@@ -214,8 +214,9 @@ struct BwdPlan {
 int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const int rc = make_plan(g, mode, &bp->fwd);
   if (rc != MAMBA_OK) return rc;
-  // one state per thread and 32-position checkpoints (the forward tile)
-  if (g->dstate > 16 || (g->dstate & (g->dstate - 1)) != 0 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  // one state per thread (16 channels x N states per workgroup, at most 512
+  // threads) and 32-position checkpoints (the forward tile)
+  if (g->dstate > 32 || (g->dstate & (g->dstate - 1)) != 0 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
   // the recompute always keeps per-direction fp32 rows (32-bit slice offsets)
   if (g->seqlen * g->dim * 4 > ((int64_t)1 << 31)) return MAMBA_ERR_UNSUPPORTED;
   const Plan& pl = bp->fwd;
@@ -225,9 +226,10 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   // Time split of the adjoint when its rows fill less than one round of
   // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
   const int64_t rows = (int64_t)bp->nblk * Bz * K;
+  const int64_t slots = N == 32 ? kBwdSlots / 2 : kBwdSlots;
   int64_t nch = 1;
-  if (rows < kBwdSlots) {
-    nch = (2 * kBwdSlots + rows - 1) / rows;
+  if (rows < slots) {
+    nch = (2 * slots + rows - 1) / rows;
     if (nch > L / kBwdMinChunk) nch = L / kBwdMinChunk;
     if (nch > 256) nch = 256;
     if (nch < 1) nch = 1;

@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WA
   constexpr int YS = TH + 4;          // padded partial row
   constexpr int QI = (N * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment
   static_assert(TS % NGP == 0 && TH % 4 == 0, "segment splits over the thread rows");
-  static_assert(N <= 16, "one state per thread");
+  static_assert(N <= 32, "one state per thread, at most 512 threads");
   constexpr bool KEEP_ABAR = MSCAN_BWD_KEEP_ABAR;
 
   __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ

@@ -220,6 +220,7 @@ int dispatch_bwd(int64_t N, const BwdParams& p, hipStream_t s) {
     case 4: return launch_bwd<TIn, 4, EXACT>(p, s);
     case 8: return launch_bwd<TIn, 8, EXACT>(p, s);
     case 16: return launch_bwd<TIn, 16, EXACT>(p, s);
+    case 32: return launch_bwd<TIn, 32, EXACT>(p, s);
     default: return MAMBA_ERR_UNSUPPORTED;
   }
 }

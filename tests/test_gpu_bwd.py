@@ -100,6 +100,11 @@ SMALL = [
     ("L32_fwd_f32_n1", W("L32_fwd", 1, 16, 32, 1, I.DIR_FWD, "f32", True, 47), True, False, False, False),
     ("grid_1x37_f32", W("grid_1x37", 1, 16, 37, 8, I.DIR_CROSS2D, "f32", True, 48, 1, 37), True, False, True, True),
     ("exact_nosoftplus_init_bf16", W("ex_nsp", 2, 32, 65, 16, I.DIR_FWD, "bf16", True, 49), False, True, True, True),
+    ("n32_fwd_bf16_init", W("n32_fwd", 2, 40, 90, 32, I.DIR_FWD, "bf16", True, 55), True, False, True, True),
+    ("n32_bidir_f32_exact", W("n32_bidir", 1, 24, 70, 32, I.DIR_BIDIR, "f32", True, 56), True, True, False, True),
+    ("n32_cross2d_bf16", W("n32_cross", 1, 16, 48, 32, I.DIR_CROSS2D, "bf16", True, 57, 6, 8), True, False, False,
+     True),
+    ("n32_split_fwd_f32", W("n32_split", 1, 16, 2300, 32, I.DIR_FWD, "f32", True, 58), True, False, True, True),
 ]
 
 
@@ -209,7 +214,7 @@ def saved_vs_recompute(name, w, xd, dout, init=None, softplus=True, exact=False)
 
 SAVED = [c for c in SMALL if c[0] in ("fwd_bf16", "fwd_f32_n4_exact_init", "bwd_bf16_n8", "bidir_f32_init",
                                       "cross2d_bf16", "cross2d_f32_n1_gated", "split_fwd_bf16", "split_bidir_f32",
-                                      "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16")]
+                                      "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16", "n32_fwd_bf16_init")]
 
 
 @pytest.mark.parametrize("case", SAVED, ids=[c[0] for c in SAVED])
