@@ -185,22 +185,32 @@ def decode_cpu_baseline(x, steps: int, budget_s: float = 3.0):
             "sample": "%d steps over all %d (b, d) rows, fp64" % (done, st.shape[0] * st.shape[1])}
 
 
-class Timer:
-    """Per-launch durations with HIP events recorded on the launch stream."""
+def timed_region(torch, stream, fn, n):
+    """n back-to-back calls with one HIP event pair on the launch stream
+    around all of them (no event between calls: an event packet between two
+    kernels delays the second by a few microseconds).  Returns (wall seconds
+    from synchronisation to synchronisation, GPU ms per call)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, e0.elapsed_time(e1) / n
 
-    def __init__(self, torch, stream, n):
-        self.torch, self.stream = torch, stream
-        self.evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
-    def run(self, fn, n):
-        for i in range(n):
-            self.evs[i][0].record(self.stream)
-            fn(i)
-            self.evs[i][1].record(self.stream)
-
-    def ms(self, n):
-        self.torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in self.evs[:n]]
+def per_call_ms(torch, stream, fn, n):
+    """Durations of n calls, each between its own HIP event pair (for the
+    median and minimum; each interval also holds the event's own latency)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
 
 
 def warm_up(torch, stream, fn, min_calls: int, min_gpu_ms: float):
@@ -235,19 +245,17 @@ def copy_ceiling(torch, stream, nbytes: int, reps: int = 10):
     with torch.cuda.stream(stream):
         for i in range(6):
             pairs[i % 3][1].copy_(pairs[i % 3][0])
-        t = Timer(torch, stream, reps)
-        t.run(lambda i: pairs[i % 3][1].copy_(pairs[i % 3][0]), reps)
-        ms = t.ms(reps)
+        _, ms = timed_region(torch, stream, lambda i: pairs[i % 3][1].copy_(pairs[i % 3][0]), reps)
     del pairs
-    s = float(np.mean(ms)) * 1e-3
+    s = ms * 1e-3
     return {"op": "torch device copy, %d bytes read + %d written per call" % (half, half),
             "us_per_call": s * 1e6, "gbs": 2 * half / s / 1e9, "frac_of_peak": 2 * half / s / 1e9 / HBM_PEAK_GBS}
 
 
 def time_config(torch, ms, I, w, steps: int, warm_ms: float, stream, cpu: bool):
     """One forward workload at full size: inputs drawn on the GPU (enough sets
-    to exceed the Infinity Cache), per-launch HIP-event timing after a warm-up
-    of at least warm_ms of GPU time, the rooflines, a copy ceiling of the same
+    to exceed the Infinity Cache), HIP-event timing of back-to-back calls after
+    a warm-up of at least warm_ms of GPU time, the rooflines, a copy ceiling of the same
     byte count, and the oracle on a channel sample."""
     dev = torch.device("cuda:0")
     alg = algorithmic_bytes(w)
@@ -268,10 +276,9 @@ def time_config(torch, ms, I, w, steps: int, warm_ms: float, stream, cpu: bool):
                     last_state=states[i % nsets], workspace=ws, stream=stream)
     with torch.cuda.stream(stream):
         wcalls, wms = warm_up(torch, stream, step, 2, warm_ms)
-        t = Timer(torch, stream, steps)
-        t.run(step, steps)
-        launch_ms = t.ms(steps)
-    avg = float(np.mean(launch_ms)) * 1e-3
+        _, region_ms = timed_region(torch, stream, step, steps)
+        launch_ms = per_call_ms(torch, stream, step, steps)
+    avg = region_ms * 1e-3
     el = w.elements
     rec = {"config": {"workload": w.name, "batch": w.batch, "dim": w.dim, "seqlen": w.seqlen, "dstate": w.dstate,
                       "dir_mode": ["fwd", "bwd", "bidir", "cross2d"][w.dir_mode], "gated": w.gated,
@@ -377,19 +384,16 @@ def main():
         # milliseconds)
         warm_calls, warm_ms = warm_up(torch, stream, step, args.warmup, args.warmup_ms)
         torch.cuda.synchronize()
-        # timed region: exactly K steps, wall clock around synchronisations,
-        # with a HIP event pair on the launch stream around each launch
-        timer = Timer(torch, stream, args.steps)
-        t0 = time.perf_counter()
-        timer.run(step, args.steps)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        launch_ms = timer.ms(args.steps)
+        # timed region: exactly K steps, wall clock around synchronisations
+        # and one HIP event pair on the launch stream around the K launches
+        wall, region_ms = timed_region(torch, stream, step, args.steps)
+        # then K more, each between its own event pair (median, minimum)
+        launch_ms = per_call_ms(torch, stream, step, args.steps)
 
     ms_step = wall * 1e3 / args.steps
     el = w.elements
     value = el / (wall / args.steps)
-    avg_launch_s = float(np.mean(launch_ms)) * 1e-3
+    avg_launch_s = region_ms * 1e-3
     alg_bytes = algorithmic_bytes(w)
     ach_elem = el / avg_launch_s / 1e9
     hbm_gbs = alg_bytes / avg_launch_s / 1e9
@@ -459,15 +463,11 @@ def main():
                 ms.conv1d_silu(cxs[i % len(cxs)]["x"], cxs[i % len(cxs)]["weight"], cxs[i % len(cxs)]["bias"],
                                out=couts[i % len(cxs)], stream=stream)
             torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.conv_steps)]
-            for i in range(args.conv_steps):
+            def cstep(i):
                 c = cxs[i % len(cxs)]
-                evs[i][0].record(stream)
                 ms.conv1d_silu(c["x"], c["weight"], c["bias"], out=couts[i % len(cxs)], stream=stream)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-        conv_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+            _, conv_ms = timed_region(torch, stream, cstep, args.conv_steps)
+        conv_s = conv_ms * 1e-3
         e = 2 if w.dtype == "bf16" else 4
         cbytes = 2 * w.batch * w.seqlen * w.dim * e + w.dim * (W + 1) * 4
         conv = {"op": "causal depthwise Conv1d (%d taps) + SiLU, [B][L][D] = [%d][%d][%d] %s"
@@ -528,14 +528,8 @@ def main():
             for i in range(3):
                 bstep(i)
             torch.cuda.synchronize()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.bwd_steps)]
-            for i in range(args.bwd_steps):
-                evs[i][0].record(stream)
-                bstep(i)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-        bwd_s = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+            _, bwd_ms = timed_region(torch, stream, bstep, args.bwd_steps)
+        bwd_s = bwd_ms * 1e-3
         # the training pass with a saved forward state: mamba_scan_fwd_save,
         # then mamba_scan_bwd reading it instead of recomputing the states
         sbytes = ms.saved_bytes(dims, w.dir_mode, w.gated)

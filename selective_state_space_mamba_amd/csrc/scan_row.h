@@ -16,7 +16,7 @@
 //     (the wave's 64 lanes read one contiguous row segment of the token-major
 //     layout), issued PD tokens ahead of use;
 //   * B_t and C_t are the same for every lane of the wave: they are read with
-//     scalar loads into SGPRs, one (token, 16-state block) ahead, from fp32
+//     scalar loads into SGPRs, one (token, 8-state block) ahead, from fp32
 //     copies padded to NP states that widen_bc_kernel writes first (so the
 //     scalar unit, which the 64 waves of a CU share, only steps addresses);
 //   * per token: Δ' = softplus(Δraw + bias)·log2 e once, then per state
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(64) scan_row_kernel(const ScanParams p) {
 #pragma unroll
   for (int s = 0; s < PD; ++s) issue(s);
 
-  // ---- B and C by scalar loads, one (position, 16-state block) ahead ----
+  // ---- B and C by scalar loads, one (position, 8-state block) ahead ----
   TokenWalk tw;  // the position being scanned
   tw.init(ws, pbeg, L);
   TokenWalk bw = tw;  // the position of the next B/C block to load
