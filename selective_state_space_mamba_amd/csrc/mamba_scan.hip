@@ -214,9 +214,12 @@ struct BwdPlan {
 int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const int rc = make_plan(g, mode, &bp->fwd);
   if (rc != MAMBA_OK) return rc;
-  // one state per thread (16 channels x N states per workgroup, at most 512
-  // threads) and 32-position checkpoints (the forward tile)
-  if (g->dstate > 32 || (g->dstate & (g->dstate - 1)) != 0 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  // one state per thread (16 channels x N states per workgroup, N rounded up
+  // to a power of two, at most 512 threads) and 32-position checkpoints
+  if (g->dstate > 32 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  // the per-element kernels of the backward (dz of several directions, the
+  // sums) take 8 consecutive channels per thread
+  if (g->dim % 8 != 0) return MAMBA_ERR_UNSUPPORTED;
   // the recompute always keeps per-direction fp32 rows (32-bit slice offsets)
   if (g->seqlen * g->dim * 4 > ((int64_t)1 << 31)) return MAMBA_ERR_UNSUPPORTED;
   const Plan& pl = bp->fwd;
@@ -226,7 +229,7 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   // Time split of the adjoint when its rows fill less than one round of
   // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
   const int64_t rows = (int64_t)bp->nblk * Bz * K;
-  const int64_t slots = N == 32 ? kBwdSlots / 2 : kBwdSlots;
+  const int64_t slots = N > 16 ? kBwdSlots / 2 : kBwdSlots;
   int64_t nch = 1;
   if (rows < slots) {
     nch = (2 * slots + rows - 1) / rows;
@@ -621,6 +624,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   q.agg_S = wsf(bp.bagg_S);
   q.agg_dsum = wsf(bp.bagg_dsum);
   q.softplus = p.softplus;
+  q.N = (int)dims->dstate;
   rc = bf16 ? (exact ? dispatch_bwd_bf16_exact(N, q, stream) : dispatch_bwd_bf16_simple(N, q, stream))
             : (exact ? dispatch_bwd_f32_exact(N, q, stream) : dispatch_bwd_f32_simple(N, q, stream));
   if (rc != MAMBA_OK) return rc;

@@ -95,6 +95,7 @@ struct BwdParams {
   int nchunks, chunk_len;   // chunks per sequence (chunk_len a multiple of 32)
   int chunk0, grid_chunks;  // chunks chunk0 .. chunk0+grid_chunks-1 are this launch's
   int Bsz, Dm, L, H, W, K, Ku, kinds, nblk_d, ntiles, softplus;
+  int N;                    // state size (the kernel may run a larger power-of-two instantiation)
 };
 
 // dz = dout·y_all·silu'(z), y_all = Σ_k y_k (ungated), silu'(z) = σ(z)·(1 + z·(1 - σ(z))),
@@ -220,11 +221,15 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
 // (The exact rule's two coefficient series need more registers than a
 // 2-wave budget: it spilled ~200 bytes per lane and ran 1.7x slower than with
 // the 1-wave budget it gets here.)
-template <typename TIn, int N, bool EXACT, bool AGG>
-__global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WAVES)
+//
+// NP: the instantiation's power-of-two state count; FULL: N == NP (N a
+// compile-time constant), else N = p.N < NP and the thread rows n >= N hold
+// no state (as the rows past N do for N < 4).
+template <typename TIn, int NP, bool FULL, bool EXACT, bool AGG>
+__global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? 1 : MSCAN_BWD_WAVES)
     scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
-  constexpr int NGP = N < 4 ? 4 : N;  // thread rows
+  constexpr int NGP = NP < 4 ? 4 : NP;  // thread rows
   constexpr int NT = CB * NGP;
   constexpr int TS = 32;              // segment (the forward checkpoint interval)
   constexpr int TH = 16;              // half segment (one butterfly)
@@ -232,16 +237,17 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WA
   constexpr int TPH = TH / NGP > 0 ? TH / NGP : 1;  // positions summed per thread per half
   constexpr int PS = TS + 4;          // padded row of a per-channel or per-state array
   constexpr int YS = TH + 4;          // padded partial row
-  constexpr int QI = (N * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment
+  constexpr int QI = (NP * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment (at most)
   static_assert(TS % NGP == 0 && TH % 4 == 0, "segment splits over the thread rows");
-  static_assert(N <= 32, "one state per thread, at most 512 threads");
+  static_assert(NP <= 32, "one state per thread, at most 512 threads");
+  const int N = FULL ? NP : p.N;
   constexpr bool KEEP_ABAR = MSCAN_BWD_KEEP_ABAR;
 
   __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ
   __shared__ __attribute__((aligned(16))) float s_u[CB * PS];    // u
   __shared__ __attribute__((aligned(16))) float s_dy[CB * PS];   // dy
-  __shared__ __attribute__((aligned(16))) float s_B[N * PS];
-  __shared__ __attribute__((aligned(16))) float s_C[N * PS];
+  __shared__ __attribute__((aligned(16))) float s_B[NP * PS];
+  __shared__ __attribute__((aligned(16))) float s_C[NP * PS];
   // Parts of dΔ and du per wave: each wave first sums its 4 state rows in
   // registers, so a (position, channel) gathers NW = NGP/4 parts.
   constexpr int NW = NGP / 4;
@@ -256,7 +262,7 @@ __global__ void __launch_bounds__(16 * (N < 4 ? 4 : N), EXACT ? 1 : MSCAN_BWD_WA
   const bool nvalid = ng < N;
   const int n = nvalid ? ng : 0;
   const uint32_t m1 = (cl & 2) ? ~0u : 0u, m0 = (cl & 1) ? ~0u : 0u;
-  const float nvf = nvalid ? 1.f : 0.f;  // rows past N (N < 4) add nothing to the state sums
+  const float nvf = nvalid ? 1.f : 0.f;  // rows past N add nothing to the state sums
 
   const int nblocks = gridDim.x;
   int bid = logical_block(blockIdx.x, nblocks, 4);

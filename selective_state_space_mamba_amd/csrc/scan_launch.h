@@ -195,34 +195,40 @@ int dispatch_step(int64_t N, const StepParams& p, hipStream_t s) {
   }
 }
 
-template <typename TIn, int N, bool EXACT>
+template <typename TIn, int NP, bool FULL, bool EXACT>
 int launch_bwd(BwdParams p, hipStream_t stream) {
-  constexpr int NT = 16 * (N < 4 ? 4 : N);
+  constexpr int NT = 16 * (NP < 4 ? 4 : NP);
   if (p.nchunks > 1) {  // aggregate pass over chunks 1.. (the carry alone: no input-term rule)
     p.chunk0 = 1;
     p.grid_chunks = p.nchunks - 1;
     const unsigned blocks = (unsigned)(p.nblk_d * p.grid_chunks * p.Bsz * p.K);
-    hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, false, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<TIn, NP, FULL, false, true>), dim3(blocks), dim3(NT), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.chunk0 = 0;
   p.grid_chunks = p.nchunks;
   const unsigned blocks = (unsigned)(p.nblk_d * p.grid_chunks * p.Bsz * p.K);
-  hipLaunchKernelGGL((scan_bwd_kernel<TIn, N, EXACT, false>), dim3(blocks), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((scan_bwd_kernel<TIn, NP, FULL, EXACT, false>), dim3(blocks), dim3(NT), 0, stream, p);
   return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
+// State sizes that are not a power of two run the next power-of-two
+// instantiation with the state count read at run time.
+template <typename TIn, int NP, bool EXACT>
+int launch_bwd_np(const BwdParams& p, hipStream_t s) {
+  if constexpr (NP <= 2) return launch_bwd<TIn, NP, true, EXACT>(p, s);
+  else return p.N == NP ? launch_bwd<TIn, NP, true, EXACT>(p, s) : launch_bwd<TIn, NP, false, EXACT>(p, s);
 }
 
 template <typename TIn, bool EXACT>
 int dispatch_bwd(int64_t N, const BwdParams& p, hipStream_t s) {
-  switch (N) {
-    case 1: return launch_bwd<TIn, 1, EXACT>(p, s);
-    case 2: return launch_bwd<TIn, 2, EXACT>(p, s);
-    case 4: return launch_bwd<TIn, 4, EXACT>(p, s);
-    case 8: return launch_bwd<TIn, 8, EXACT>(p, s);
-    case 16: return launch_bwd<TIn, 16, EXACT>(p, s);
-    case 32: return launch_bwd<TIn, 32, EXACT>(p, s);
-    default: return MAMBA_ERR_UNSUPPORTED;
-  }
+  if (N < 1 || N > 32) return MAMBA_ERR_UNSUPPORTED;
+  if (N <= 1) return launch_bwd_np<TIn, 1, EXACT>(p, s);
+  if (N <= 2) return launch_bwd_np<TIn, 2, EXACT>(p, s);
+  if (N <= 4) return launch_bwd_np<TIn, 4, EXACT>(p, s);
+  if (N <= 8) return launch_bwd_np<TIn, 8, EXACT>(p, s);
+  if (N <= 16) return launch_bwd_np<TIn, 16, EXACT>(p, s);
+  return launch_bwd_np<TIn, 32, EXACT>(p, s);
 }
 
 #endif  // MSCAN_INSTANTIATE

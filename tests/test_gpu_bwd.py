@@ -105,6 +105,11 @@ SMALL = [
     ("n32_cross2d_bf16", W("n32_cross", 1, 16, 48, 32, I.DIR_CROSS2D, "bf16", True, 57, 6, 8), True, False, False,
      True),
     ("n32_split_fwd_f32", W("n32_split", 1, 16, 2300, 32, I.DIR_FWD, "f32", True, 58), True, False, True, True),
+    ("n3_fwd_f32_init", W("n3_fwd", 2, 24, 70, 3, I.DIR_FWD, "f32", True, 59), True, False, True, True),
+    ("n12_bidir_bf16", W("n12_bidir", 1, 40, 66, 12, I.DIR_BIDIR, "bf16", True, 60), True, False, False, True),
+    ("n24_cross2d_f32_exact", W("n24_cross", 1, 16, 42, 24, I.DIR_CROSS2D, "f32", True, 62, 6, 7), True, True,
+     False, True),
+    ("n20_split_bwd_bf16", W("n20_split", 1, 16, 2200, 20, I.DIR_BWD, "bf16", True, 63), True, False, True, True),
 ]
 
 
@@ -214,7 +219,8 @@ def saved_vs_recompute(name, w, xd, dout, init=None, softplus=True, exact=False)
 
 SAVED = [c for c in SMALL if c[0] in ("fwd_bf16", "fwd_f32_n4_exact_init", "bwd_bf16_n8", "bidir_f32_init",
                                       "cross2d_bf16", "cross2d_f32_n1_gated", "split_fwd_bf16", "split_bidir_f32",
-                                      "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16", "n32_fwd_bf16_init")]
+                                      "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16", "n32_fwd_bf16_init",
+                                      "n3_fwd_f32_init", "n12_bidir_bf16")]
 
 
 @pytest.mark.parametrize("case", SAVED, ids=[c[0] for c in SAVED])
