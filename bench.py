@@ -428,6 +428,16 @@ def main():
                 stepper(ut, dt_, Bt, Ct, zt, out=o)
             torch.cuda.synchronize()
             sdec_s = time.perf_counter() - t0
+            # and with static per-token buffers bound once (one C call per step)
+            stepper.bind(ut, dt_, Bt, Ct, zt, out=o)
+            for _ in range(10):
+                stepper.step()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.decode_steps):
+                stepper.step()
+            torch.cuda.synchronize()
+            bdec_s = time.perf_counter() - t0
         # the same loop captured once as a HIP graph and replayed (no host
         # work per step): the kernel-bound rate of the decode loop
         graph = torch.cuda.CUDAGraph()
@@ -447,6 +457,7 @@ def main():
         del graph
         decode = {"steps": args.decode_steps, "us_per_step": dec_s * 1e6 / args.decode_steps,
                   "stepper_us_per_step": sdec_s * 1e6 / args.decode_steps,
+                  "bound_stepper_us_per_step": bdec_s * 1e6 / args.decode_steps,
                   "graph_us_per_step": gdec_s * 1e6 / args.decode_steps,
                   "state_bytes_per_step": 2 * w.batch * w.dim * w.dstate * 4,
                   "elements_per_step": w.batch * w.dim * w.dstate,

@@ -437,10 +437,38 @@ class ScanStepper:
         self._bn = torch.Size((Bsz, N))
         self._dtype = dtype
         self._device = dev
+        self._args = None
 
     def _ok(self, t, name, shape):
         if not (t.shape == shape and t.dtype == self._dtype and t.is_contiguous() and t.device == self._device):
             _check(t, name, shape, self._dtype, self._device)  # raises with the reason
+
+    def bind(self, u_t, delta_t, B_t, C_t, z_t=None, *, out):
+        """Checks and keeps one set of per-token buffers for step(): a decode
+        loop that writes each token's u, delta, B, C (and z) into these same
+        tensors then makes one C call per token, with no per-call checks."""
+        bd, bn = self._bd, self._bn
+        self._ok(u_t, "u_t", bd)
+        self._ok(delta_t, "delta_t", bd)
+        self._ok(B_t, "B_t", bn)
+        self._ok(C_t, "C_t", bn)
+        if z_t is not None:
+            self._ok(z_t, "z_t", bd)
+        self._ok(out, "out", bd)
+        self._bound = (u_t, delta_t, B_t, C_t, z_t, out)  # kept alive with their pointers
+        self._args = (self._state, u_t.data_ptr(), delta_t.data_ptr(), self._A, B_t.data_ptr(), C_t.data_ptr(),
+                      self._D, None if z_t is None else z_t.data_ptr(), self._bias, self._dims_ref, out.data_ptr(),
+                      self._stream)
+        return self
+
+    def step(self):
+        """One step on the bound buffers (bind() first); returns the bound out."""
+        if self._args is None:
+            raise RuntimeError("ScanStepper.step() needs bind() first")
+        rc = self._lib.mamba_scan_step(*self._args)
+        if rc != MAMBA_OK:
+            raise MambaError(rc, "mamba_scan_step")
+        return self._bound[5]
 
     def __call__(self, u_t, delta_t, B_t, C_t, z_t=None, *, out):
         """One step: u_t, delta_t, z_t, out [B][D]; B_t, C_t [B][N]."""

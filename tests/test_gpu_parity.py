@@ -385,6 +385,21 @@ def test_stepper_is_scan_step(N, dtype):
         assert t.equal(oa, ob), s
     t.cuda.synchronize()
     assert t.equal(st_a, st_b)
+    # bound buffers: each token copied into the same tensors, one call per step
+    st_c = st.contiguous().clone()
+    bound = {k: t.empty_like(tail[k][0]) for k in tail}
+    ob = t.empty_like(tail["u"][0])
+    stepper_c = ms.ScanStepper(st_c, xd["A"], xd["D"], xd["delta_bias"], dtype=tail["u"].dtype)
+    stepper_c.bind(bound["u"], bound["delta"], bound["B"], bound["C"], bound["z"], out=ob)
+    st_a = st.contiguous().clone()
+    for s in range(steps):
+        for k in tail:
+            bound[k].copy_(tail[k][s])
+        a = {k: tail[k][s].clone() for k in tail}  # (fresh allocations: 16-byte aligned)
+        oa = ms.scan_step(st_a, a["u"], a["delta"], xd["A"], a["B"], a["C"], xd["D"], a["z"], xd["delta_bias"])
+        assert t.equal(oa, stepper_c.step()), s
+    t.cuda.synchronize()
+    assert t.equal(st_a, st_c)
     bad = tail["B"][0][:, :N - 1].contiguous()
     with pytest.raises(ValueError):
         stepper(tail["u"][0], tail["delta"][0], bad, tail["C"][0], tail["z"][0], out=t.empty_like(tail["u"][0]))
