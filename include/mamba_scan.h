@@ -218,7 +218,8 @@ MAMBA_API size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_
 /*
  * Bytes of the saved forward state that mamba_scan_fwd_save writes and
  * mamba_scan_bwd can read in place of its forward recompute: the state before
- * every 32-position tile, [K][B][ceil(L/32)][D][N] float32, and, when gated is
+ * every 16th position (every 32nd when N is above 16), [K][B][ceil(L/16 or
+ * 32)][D][N] float32, and, when gated is
  * nonzero (a scan with z whose dz will be asked for), after it (at a 256-byte
  * aligned offset) the ungated per-direction outputs [K][B][L][D] float32.
  * A pure function of its arguments; (size_t)-1 when the arguments are invalid

@@ -198,7 +198,7 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 
 // Workspace of the backward pass, in this order (each region 256-byte aligned):
 // the forward recompute's time-split carries, the per-direction fp32 output
-// rows, state checkpoints every 32 positions, the per-channel-block partial
+// rows, state checkpoints every 16 (N above 16: 32) positions, the per-channel-block partial
 // sums of dB and dC, the per-direction du of the cross scan, the per-chunk
 // and per-batch partial sums of dA, dD and ddelta_bias, and the adjoint's
 // time-split carries.
@@ -207,7 +207,7 @@ constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per 
 constexpr int kBwdMinChunk = 1024;  // shortest time chunk of a split adjoint
 struct BwdPlan {
   Plan fwd;
-  int nblk, ntiles, nchunks, chunk_len;
+  int nblk, ntiles, every, nchunks, chunk_len;
   size_t agg, ws_y, ckpt, dB, dC, du, dA, dD, dbias, bagg_S, bagg_dsum, total;
 };
 
@@ -215,7 +215,8 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const int rc = make_plan(g, mode, &bp->fwd);
   if (rc != MAMBA_OK) return rc;
   // one state per thread (16 channels x N states per workgroup, N rounded up
-  // to a power of two, at most 512 threads) and 32-position checkpoints
+  // to a power of two, at most 512 threads) and checkpoints at multiples of
+  // the tile
   if (g->dstate > 32 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
   // the per-element kernels of the backward (dz of several directions, the
   // sums) take 8 consecutive channels per thread
@@ -225,7 +226,10 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const Plan& pl = bp->fwd;
   const int64_t K = pl.K, Bz = g->batch, L = g->seqlen, Dm = g->dim, N = g->dstate;
   bp->nblk = (int)((Dm + kBwdBlock - 1) / kBwdBlock);
-  bp->ntiles = (int)((L + kTile - 1) / kTile);
+  // checkpoint interval = the adjoint's segment: 16 positions, 32 above 16
+  // states (the adjoint kernel's segment for 32 thread rows)
+  bp->every = N > 16 ? 32 : 16;
+  bp->ntiles = (int)((L + bp->every - 1) / bp->every);
   // Time split of the adjoint when its rows fill less than one round of
   // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
   const int64_t rows = (int64_t)bp->nblk * Bz * K;
@@ -366,7 +370,7 @@ int dispatch_fwd(const mamba_dims* dims, const ScanParams& p, const Plan& pl, hi
 }
 
 // Saved forward state (mamba_scan_fwd_save -> mamba_scan_bwd): the state
-// before every 32-position tile, [K][B][ceil(L/32)][D][N] fp32, then, for a
+// before every 16th position (32nd above 16 states), [K][B][ntiles][D][N] fp32, then, for a
 // gated scan, the ungated per-direction rows [K][B][L][D] fp32 (dz needs them).
 struct SavedLayout {
   BwdPlan bp;
@@ -522,6 +526,7 @@ int mamba_scan_fwd_save(const void* u, const void* delta, const float* A, const 
   p.last_state = last_state;
   p.ckpt = reinterpret_cast<float*>(sv);
   p.ckpt_tiles = sl.bp.ntiles;
+  p.ckpt_every = sl.bp.every;
   return dispatch_fwd(dims, p, pl, stream);
 }
 
@@ -570,6 +575,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
     p.last_state = nullptr;
     p.ckpt = wsf(bp.ckpt);
     p.ckpt_tiles = bp.ntiles;
+    p.ckpt_every = bp.every;
     rc = dispatch_fwd(dims, p, pl, stream);
     if (rc != MAMBA_OK) return rc;
   }

@@ -15,12 +15,13 @@
 //   dB_t = Σ_d λ·(Δ or c)·u,  dC_t = Σ_d dy_t·h_p,  dD = Σ dy·u
 //   ddelta = dΔ·σ(x) (softplus) = dΔ·(1 - e^{-Δ}),  ddelta_bias = Σ ddelta
 //   dinit = Ā_0·λ_0
-// The forward pass with state checkpoints every 32 positions runs first
+// The forward pass with state checkpoints every 16 positions (32 above 16
+// states) runs first
 // (scan_chunk_kernel with ScanParams::ckpt); scan_bwd_kernel then walks each
-// (direction, batch, 16-channel block) backwards one 32-position segment at a
-// time: it recomputes the segment's states from its checkpoint into
-// registers, then runs the adjoint recurrence over the two 16-position
-// halves.  Sums over states go through LDS (like the forward readout); sums
+// (direction, batch, 16-channel block) backwards one segment (16 positions,
+// 32 for N above 16) at a time: it recomputes the segment's states from its
+// checkpoint into registers, then runs the adjoint recurrence over its
+// 16-position halves.  Sums over states go through LDS (like the forward readout); sums
 // over the block's 16 channels (dB, dC) through a register butterfly across
 // each 16-lane row; sums over blocks and batches in bwd_sum_kernel.
 #pragma once
@@ -31,6 +32,9 @@ namespace mscan {
 
 #ifndef MSCAN_BWD_WAVES
 #define MSCAN_BWD_WAVES 2  // waves per SIMD the adjoint kernel's register budget is sized for (3 spills)
+#endif
+#ifndef MSCAN_BWD_SEG
+#define MSCAN_BWD_SEG 16  // segment length (the forward's checkpoint interval) up to 16 states
 #endif
 #ifndef MSCAN_BWD_KEEP_ABAR
 #define MSCAN_BWD_KEEP_ABAR 1  // 1: keep the segment's e^{ΔA} from the recompute (32 registers) instead of recomputing
@@ -73,7 +77,7 @@ struct BwdParams {
   const void* C;
   const float* D;           // may be null
   const float* delta_bias;  // may be null
-  const float* ckpt;        // [K][Bsz][ntiles][Dm][N] states at every 32-position tile start
+  const float* ckpt;        // [K][Bsz][ntiles][Dm][N] states before every segment (TS positions)
   const void* dout;         // [Bsz][L][Dm]
   const void* z;            // [Bsz][L][Dm] or null (no gate)
   const float* ws_y;        // [K][Bsz][L][Dm] ungated output rows of the forward recompute, or null
@@ -231,7 +235,11 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? 1 : MSCAN_BWD_
   constexpr int CB = 16;
   constexpr int NGP = NP < 4 ? 4 : NP;  // thread rows
   constexpr int NT = CB * NGP;
-  constexpr int TS = 32;              // segment (the forward checkpoint interval)
+  // segment = the forward's checkpoint interval: 16 positions (registers for
+  // 16 recomputed states and decays per thread: 146 VGPRs at N = 16, 3 waves
+  // per SIMD, against 206 and 2 waves with 32), 32 for 32 thread rows (each
+  // row stages one position per segment)
+  constexpr int TS = NGP > MSCAN_BWD_SEG ? NGP : MSCAN_BWD_SEG;
   constexpr int TH = 16;              // half segment (one butterfly)
   constexpr int TPS = TS / NGP;       // positions staged per thread per segment
   constexpr int TPH = TH / NGP > 0 ? TH / NGP : 1;  // positions summed per thread per half
@@ -431,7 +439,7 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? 1 : MSCAN_BWD_
 
     // ---- the adjoint over the two halves, later half first ----
 #pragma unroll
-    for (int half = 1; half >= 0; --half) {
+    for (int half = TS / TH - 1; half >= 0; --half) {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int qt = 1; qt >= 0; --qt) {

@@ -75,7 +75,8 @@ struct ScanParams {
   float* last_state;        // [Bsz][K][D][N] or null
   float* agg_state;         // [K][Bsz][nchunks-1][D][N]
   float* agg_dsum;          // [K][Bsz][nchunks-1][D]
-  float* ckpt;              // [K][Bsz][ckpt_tiles][D][N] state at every tile start, or null
+  float* ckpt;              // [K][Bsz][ckpt_tiles][D][N] state before every ckpt_every-th
+                            // position (ckpt_every 16 or 32, a divisor of the tile), or null
   float* bcw;               // row kernel: B then C widened to fp32 rows of NP values, [Bsz][K][L][NP] each
   int Bsz, Dm, L, H, W;
   int N;                    // state size (the row kernel may run a larger power-of-two instantiation)
@@ -86,7 +87,8 @@ struct ScanParams {
   int grid_chunks;          // chunks covered by this launch's grid
   int nblk_d;               // channel blocks of 64
   int softplus;
-  int ckpt_tiles;           // tiles of TT positions per sequence (checkpoint rows)
+  int ckpt_tiles;           // checkpoint rows per sequence: ceil(L / ckpt_every)
+  int ckpt_every;           // positions between checkpoints
   int prio;                 // 1: the scan loop runs at raised wave priority (16-channel blocks)
   int kbase;                // first direction of this launch's grid
   int fold;                 // 1: the launch's direction (the last, k = K-1) adds the rows of
@@ -357,12 +359,16 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   float dsum = 0.f;
   // one tile: barrier, scan, barrier, epilogue (the next tile is staged by the caller)
   auto process_tile = [&](int p0) {
-    if (!AGG && p.ckpt && dvalid) {
-      // the state before tile p0, for the recomputation of the backward pass
-      float* S = p.ckpt + ((((int64_t)k * p.Bsz + b) * p.ckpt_tiles + p0 / TT) * D + d) * N + ng * G;
+    // the state before position pos, for the recomputation of the backward
+    // pass (at the tile start, and inside the tile every ckpt_every positions)
+    auto checkpoint = [&](int pos) {
+      if (!AGG && p.ckpt && dvalid && pos < pend) {
+        float* S = p.ckpt + ((((int64_t)k * p.Bsz + b) * p.ckpt_tiles + pos / p.ckpt_every) * D + d) * N + ng * G;
 #pragma unroll
-      for (int j = 0; j < G; ++j) S[j] = h[j];
-    }
+        for (int j = 0; j < G; ++j) S[j] = h[j];
+      }
+    };
+    checkpoint(p0);
     __syncthreads();
     const int tlen = min(TT, pend - p0);
     // Rows of the tile past the chunk end were staged as Δ' = 0, Δu = 0, B = C = 0:
@@ -448,6 +454,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         if (4 * q < tend) {
           if (q + PDQ < NQ) read_ops(ring[(q + PDQ) % (PDQ + 1)], 4 * (q + PDQ));
           quad(ring[q % (PDQ + 1)], 4 * q);
+          if (4 * q + 4 == 16 && TT > 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
         }
       }
     } else {
@@ -461,6 +468,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
           if (tt + 4 < tend) {
             read_ops(o0, min(tt + 8, TT - 4));  // the last prefetch re-reads rows that go unused
             quad(o1, tt + 4);
+            if (tt + 8 == 16 && TT > 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
           }
         }
       }

@@ -269,9 +269,10 @@ __global__ void __launch_bounds__(64) scan_row_kernel(const ScanParams p) {
     constexpr bool SP = decltype(softplus_tag)::value;
     auto do_step = [&](const int j, const int step, const bool refill) {
       const int pp = pbeg + step;
-      if (ckpt && (pp % 32) == 0 && dvalid) {
-        // the state before this 32-position tile, for the backward pass
-        float* S = p.ckpt + ((((int64_t)k * p.Bsz + b) * p.ckpt_tiles + pp / 32) * D + d) * N;
+      if (ckpt && (pp & (p.ckpt_every - 1)) == 0 && dvalid) {
+        // the state before this position, every ckpt_every (a power of two)
+        // positions, for the backward pass
+        float* S = p.ckpt + ((((int64_t)k * p.Bsz + b) * p.ckpt_tiles + pp / p.ckpt_every) * D + d) * N;
 #pragma unroll
         for (int n = 0; n < NP; ++n)
           if (FULL || n < N) S[n] = h[n];

@@ -193,11 +193,14 @@ def test_saved_state_size_and_fwd_save_validation(lib):
     L, Dm, N, Bz = 100, 64, 16, 2
     d = dims()
     ck = ms.saved_bytes(d, ms.DIR_FWD, False)
-    # the state before each of the ceil(L/32) tiles, 256-byte aligned, then the fp32 output rows
-    assert ck == (Bz * 4 * Dm * N * 4 + 255) // 256 * 256
+    # the state before every 16th position (ceil(L/16) of them at N <= 16), 256-byte aligned, then the
+    # fp32 output rows
+    assert ck == (Bz * 7 * Dm * N * 4 + 255) // 256 * 256
     assert ms.saved_bytes(d, ms.DIR_FWD, True) == ck + Bz * L * Dm * 4
     cross = dims(seqlen=96, height=8, width=12)
-    assert ms.saved_bytes(cross, ms.DIR_CROSS2D, True) == 4 * Bz * 3 * Dm * N * 4 + 4 * Bz * 96 * Dm * 4
+    assert ms.saved_bytes(cross, ms.DIR_CROSS2D, True) == 4 * Bz * 6 * Dm * N * 4 + 4 * Bz * 96 * Dm * 4
+    # above 16 states, every 32nd position
+    assert ms.saved_bytes(dims(dstate=32), ms.DIR_FWD, False) == (Bz * 4 * Dm * 32 * 4 + 255) // 256 * 256
     for bad in (dims(dstate=64), dims(dstate=33), dims(seqlen=0), dims(dim=60)):
         with pytest.raises(ms.MambaError):
             ms.saved_bytes(bad, ms.DIR_FWD, False)
