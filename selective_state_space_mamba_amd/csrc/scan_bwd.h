@@ -33,6 +33,9 @@ namespace mscan {
 #ifndef MSCAN_BWD_WAVES
 #define MSCAN_BWD_WAVES 2  // waves per SIMD the adjoint kernel's register budget is sized for (3 spills)
 #endif
+#ifndef MSCAN_BWD_WAVES_EXACT
+#define MSCAN_BWD_WAVES_EXACT 1  // the same for the exact rule (with 16-position segments it fits 198 VGPRs anyway)
+#endif
 #ifndef MSCAN_BWD_SEG
 #define MSCAN_BWD_SEG 16  // segment length (the forward's checkpoint interval) up to 16 states
 #endif
@@ -222,15 +225,15 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
 // pass then starts chunk c from the fold over the later chunks j,
 // carry <- S_j + e^{A·ΣΔ_j}·carry (the carry's dependence on its start value
 // is the product of the chunk's decays).
-// (The exact rule's two coefficient series need more registers than a
-// 2-wave budget: it spilled ~200 bytes per lane and ran 1.7x slower than with
-// the 1-wave budget it gets here.)
+// (The exact rule's two coefficient series needed more registers than a
+// 2-wave budget with 32-position segments; it keeps a 1-wave budget, within
+// which the 16-position segment's kernel takes 198 VGPRs: 2 waves per SIMD.)
 //
 // NP: the instantiation's power-of-two state count; FULL: N == NP (N a
 // compile-time constant), else N = p.N < NP and the thread rows n >= N hold
 // no state (as the rows past N do for N < 4).
 template <typename TIn, int NP, bool FULL, bool EXACT, bool AGG>
-__global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? 1 : MSCAN_BWD_WAVES)
+__global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVES_EXACT : MSCAN_BWD_WAVES)
     scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
   constexpr int NGP = NP < 4 ? 4 : NP;  // thread rows
