@@ -15,6 +15,9 @@
 //   dB_t = Σ_d λ·(Δ or c)·u,  dC_t = Σ_d dy_t·h_p,  dD = Σ dy·u
 //   ddelta = dΔ·σ(x) (softplus) = dΔ·(1 - e^{-Δ}),  ddelta_bias = Σ ddelta
 //   dinit = Ā_0·λ_0
+// With the simplified rule (B̄ = Δ·B) the channel's u and Δ factor out of the
+// state sums: dΔ_p = Σ_n λ h_{p-1} A Ā + u·Σ_n λ B_n and du = Δ·Σ_n λ B_n + D·dy,
+// so the per-state terms are λ h_{p-1} Ā A_n and λ B_n (and Δ·u is staged once).
 // The forward pass with state checkpoints every 16 positions (32 above 16
 // states) runs first
 // (scan_chunk_kernel with ScanParams::ckpt); scan_bwd_kernel then walks each
@@ -257,6 +260,8 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ
   __shared__ __attribute__((aligned(16))) float s_u[CB * PS];    // u
   __shared__ __attribute__((aligned(16))) float s_dy[CB * PS];   // dy
+  // Δ·u, shared by the channel's states (the simplified rule's input term)
+  __shared__ __attribute__((aligned(16))) float s_du[EXACT ? 4 : CB * PS];
   __shared__ __attribute__((aligned(16))) float s_B[NP * PS];
   __shared__ __attribute__((aligned(16))) float s_C[NP * PS];
   // Parts of dΔ and du per wave: each wave first sums its 4 state rows in
@@ -355,8 +360,13 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
       const int tt = ng * TPS + i;
       const float okf = (p0 + tt < L && dvalid) ? 1.f : 0.f;
       const float x = to_f32(r.dl[i]) + bias;
-      s_dt[cl * PS + tt] = (p.softplus ? softplus_log2(x) * kLn2 : x) * okf;
-      if constexpr (!AGG) s_u[cl * PS + tt] = to_f32(r.u[i]) * okf;
+      const float dtv = (p.softplus ? softplus_log2(x) * kLn2 : x) * okf;
+      s_dt[cl * PS + tt] = dtv;
+      if constexpr (!AGG) {
+        const float uu = to_f32(r.u[i]) * okf;
+        s_u[cl * PS + tt] = uu;
+        if constexpr (!EXACT) s_du[cl * PS + tt] = dtv * uu;
+      }
       // dy = dout·silu(z); with one direction also dz = dout·y·silu'(z)
       const float g = to_f32(r.go[i]);
       float dyv = g;
@@ -427,11 +437,14 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
 #pragma unroll
       for (int s = 0; s < TS; ++s) {
         const float dt = s_dt[cl * PS + s];
-        const float uu = s_u[cl * PS + s];
         const float Bv = s_B[n * PS + s];
         const float a = ex2(dt * Al2);
-        const float c = EXACT ? zoh_coef(a, dt * Anat, dt, invA) : dt;
-        h = __builtin_fmaf(a, h, c * uu * Bv);
+        if constexpr (EXACT) {
+          const float c = zoh_coef(a, dt * Anat, dt, invA);
+          h = __builtin_fmaf(a, h, c * s_u[cl * PS + s] * Bv);
+        } else {
+          h = __builtin_fmaf(a, h, s_du[cl * PS + s] * Bv);  // (Δ·u)·B
+        }
         hs[s] = h;
         if constexpr (KEEP_ABAR) as[s] = a;
       }
@@ -456,7 +469,6 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
             const int sq = s4 + r;                 // step within the quarter
             const int s = half * TH + qt * 8 + sq;  // step within the segment
             const float dt = s_dt[cl * PS + s];
-            const float uu = s_u[cl * PS + s];
             const float dyv = s_dy[cl * PS + s];
             const float Bv = s_B[n * PS + s];
             const float Cv = s_C[n * PS + s];
@@ -466,6 +478,7 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
             const float ga = l * hp;
             const float lB = l * Bv;
             if constexpr (EXACT) {
+              const float uu = s_u[cl * PS + s];
               const float x = dt * Anat;
               const float c = zoh_coef(a, x, dt, invA);
               // dc/dΔ = e^{ΔA}; dc/dA from zoh_coef_dA
@@ -473,12 +486,17 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
               pu4[r] = lB * c;
               dA_acc = __builtin_fmaf(lB * zoh_coef_dA(a, x, dt, c, invA), uu, dA_acc);
               pBC[sq] = l * c * uu;
+              dA_acc = __builtin_fmaf(ga * dt, a, dA_acc);
             } else {
-              pd4[r] = __builtin_fmaf(ga * Anat, a, lB * uu);
-              pu4[r] = lB * dt;
-              pBC[sq] = l * dt * uu;
+              // dΔ = Σ_n λ h_{p-1} Ā A_n + u·Σ_n λ B_n and du = Δ·Σ_n λ B_n:
+              // the per-state parts are λ h_{p-1} Ā A_n and λ B_n, the
+              // channel's u and Δ enter once per position in the sums below
+              const float gaa = ga * a;
+              pd4[r] = gaa * Anat;
+              pu4[r] = lB;
+              dA_acc = __builtin_fmaf(gaa, dt, dA_acc);
+              pBC[sq] = l * s_du[cl * PS + s];  // λ·(Δ·u)
             }
-            dA_acc = __builtin_fmaf(ga * dt, a, dA_acc);
             pBC[8 + sq] = dyv * hs[s];
             carry = a * l;
           }
@@ -515,6 +533,10 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
           const float dt = s_dt[cl * PS + s];
           const float uu = s_u[cl * PS + s];
           const float dyv = s_dy[cl * PS + s];
+          if constexpr (!EXACT) {  // duu holds Σ_n λ B_n
+            dd = __builtin_fmaf(uu, duu, dd);
+            duu *= dt;
+          }
           // softplus'(x) = sigmoid(x) = 1 - e^{-Δ}
           const float dx = p.softplus ? dd * (1.0f - ex2(-dt * kLog2e)) : dd;
           duu = __builtin_fmaf(Dd, dyv, duu);
