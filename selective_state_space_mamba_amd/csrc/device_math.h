@@ -229,6 +229,12 @@ struct Small<float, 1> {
 
 // ---- buffer-resource access: SGPR descriptor + scalar row offset + per-lane offset ----
 // Raw buffer descriptor over `bytes` bytes at `base` (stride 0; word 3 as for gfx9 raw buffers).
+// A buffer offset past every slice this library addresses through a
+// descriptor (each at most 2^31 bytes, by the plans' limits): a raw buffer
+// access there is out of range, so a store is dropped and a load returns 0.
+// A descriptor of 0 bytes drops every access the same way.
+constexpr uint32_t kDrop = 0x80000000u;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }

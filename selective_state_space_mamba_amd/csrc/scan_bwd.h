@@ -319,6 +319,29 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   const bool own = nvalid && dvalid;  // this thread's (channel, state) exists
   const int64_t ck_off = own ? (int64_t)d * N + n : 0;
 
+  // Stores inside the segment loop go through buffer descriptors over this
+  // workgroup's slices (each at most 2^31 bytes: the plan's limits), every
+  // one issued unconditionally: a lane with nothing to store takes the offset
+  // kDrop, past its slice, and a descriptor of 0 bytes drops every lane (dz
+  // without dz_here, the du layout not in use).  With no store under a branch
+  // the compiler counts the memory operations issued after a prefetch
+  // exactly, so staging waits for the prefetched rows only, not for the
+  // stores issued since.
+  constexpr uint32_t ES = sizeof(TIn);
+  const uint32_t rowb = (uint32_t)D * ES;  // bytes per token row
+  const uint32_t slice = (uint32_t)((int64_t)L * D * ES);
+  const bool du32 = p.du_part != nullptr;
+  const auto rs_dz = make_rsrc(p.dz_here ? static_cast<TIn*>(p.dz) + (int64_t)b * L * D : nullptr,
+                               p.dz_here ? slice : 0u);
+  const auto rs_ddt = make_rsrc(static_cast<TIn*>(p.ddelta) + (int64_t)(b * p.K + k) * L * D, slice);
+  const auto rs_du = make_rsrc(du32 ? nullptr : static_cast<TIn*>(p.du) + (int64_t)(b * p.Ku + ku) * L * D,
+                               du32 ? 0u : slice);
+  const auto rs_du32 = make_rsrc(du32 ? p.du_part + ((int64_t)k * p.Bsz + b) * L * D : nullptr,
+                                 du32 ? (uint32_t)((int64_t)L * D * 4) : 0u);
+  const int64_t bc_slice = (((int64_t)dblk * p.Bsz + b) * p.K + k) * L * N;
+  const auto rs_dB = make_rsrc(p.dB_part + bc_slice, (uint32_t)((int64_t)L * N * 4));
+  const auto rs_dC = make_rsrc(p.dC_part + bc_slice, (uint32_t)((int64_t)L * N * 4));
+
   const float Anat = own ? p.A[((int64_t)k * D + d) * N + n] : 0.f;
   const float Al2 = Anat * kLog2e;  // e^{ΔA} = 2^{Δ·A·log2 e}
   const float invA = Anat != 0.f ? 1.0f / Anat : 0.f;
@@ -369,14 +392,17 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
       }
       // dy = dout·silu(z); with one direction also dz = dout·y·silu'(z)
       const float g = to_f32(r.go[i]);
-      float dyv = g;
+      float dyv = g, dzv = 0.f;
       if (gated) {
         const float zz = to_f32(r.zr[i]);
         const float sg = rcp(1.0f + ex2(-zz * kLog2e));
         dyv = g * zz * sg;
-        if (!AGG && p.dz_here && p0 + tt < L && dvalid)
-          store1(static_cast<TIn*>(p.dz) + ((int64_t)b * L + token(p0 + tt)) * D + d,
-                 g * r.y[i] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f));
+        if constexpr (!AGG) dzv = g * r.y[i] * sg * __builtin_fmaf(zz, 1.0f - sg, 1.0f);
+      }
+      if constexpr (!AGG) {
+        const int pp = min(p0 + tt, L - 1);
+        const uint32_t off = __umul24((uint32_t)token(pp), rowb) + (uint32_t)dc * ES;
+        store_out(dzv, rs_dz, (gated && p0 + tt < L && dvalid) ? off : kDrop, 0u, (TIn*)nullptr);
       }
       s_dy[cl * PS + tt] = dyv * okf;
     }
@@ -404,19 +430,29 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   }
   float dA_acc = 0.f, dD_acc = 0.f, dbias_acc = 0.f, dsum = 0.f;
 
+  // The loop is rotated: a segment's rows are loaded at the start of the
+  // segment after it (in walk order) and staged at its end, so no load in
+  // flight crosses the loop's back edge.  (Every read of the staging arrays
+  // comes before the last barrier of a segment, so staging needs no barrier
+  // of its own.)  Wave priorities: the recompute and the adjoint steps 1,
+  // staging and the per-position sums 0 (the cross scan's backward: 2.72 ->
+  // 2.65 ms).
   Raw raw;
-  load_seg(seg_hi, raw);
-  // (Every read of the staging arrays comes before the last barrier of the
-  // previous segment, so staging needs no barrier of its own.)
-  for (int seg = seg_hi; seg >= seg_lo; --seg) {
-    const int p0 = seg * TS;
-    // Wave priorities: the recompute and the adjoint steps 1, staging and the
-    // per-position sums 0 (the cross scan's backward: 2.72 -> 2.65 ms).
+  float h0n = 0.f;
+  auto stage = [&](int seg) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(0);
     stage_seg(seg, raw);
-    const float h0 = (!AGG && own) ? raw.h0 : 0.f;  // (before the prefetch overwrites raw)
+    // the checkpoint is waited for here, with the staged rows
+    h0n = (!AGG && own) ? raw.h0 : 0.f;
+    asm volatile("" ::"v"(h0n));
+  };
+  load_seg(seg_hi, raw);
+  stage(seg_hi);
+  for (int seg = seg_hi; seg >= seg_lo; --seg) {
+    const int p0 = seg * TS;
+    const float h0 = h0n;
     __syncthreads();
-    if (seg > seg_lo) load_seg(seg - 1, raw);
+    load_seg(seg > seg_lo ? seg - 1 : seg, raw);  // (the last segment reloads its own rows, unused)
 
     if constexpr (AGG) {
 #pragma unroll 8
@@ -510,49 +546,55 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
         // cl, lane cl >= 8 with dC of step cl - 8
         const float sBC = row_sum_transpose16(pBC, m1, m0);
         const int pp = p0 + half * TH + qt * 8 + (cl & 7);
-        if (nvalid && pp < L) {
-          const int64_t off = ((((int64_t)dblk * p.Bsz + b) * p.K + k) * L + token(pp)) * N + n;
-          (cl < 8 ? p.dB_part : p.dC_part)[off] = sBC;
-        }
+        const uint32_t off = __umul24((uint32_t)token(min(pp, L - 1)), (uint32_t)N * 4u) + (uint32_t)n * 4u;
+        const bool ok = nvalid && pp < L;
+        buf_store(sBC, rs_dB, (ok && cl < 8) ? off : kDrop, 0u);
+        buf_store(sBC, rs_dC, (ok && cl >= 8) ? off : kDrop, 0u);
       }
       __syncthreads();
       // ---- sums over states, per (position, channel) ----
       __builtin_amdgcn_s_setprio(0);
+      // (with 32 thread rows, rows 16..31 have no position of the half: they
+      // repeat the last one, add nothing and store nothing)
+      constexpr bool ALLROWS = TPH * NGP <= TH;
 #pragma unroll
       for (int i = 0; i < TPH; ++i) {
-        const int sh = ng * TPH + i;  // position within the half
-        if (sh < TH) {
-          const int s = half * TH + sh;
-          const int pp = p0 + s;
-          float dd = 0.f, duu = 0.f;
+        const int sh0 = ng * TPH + i;  // position within the half
+        const bool hv = ALLROWS || sh0 < TH;
+        const int sh = hv ? sh0 : TH - 1;
+        const float hf = hv ? 1.f : 0.f;
+        const int s = half * TH + sh;
+        const int pp = p0 + s;
+        float dd = 0.f, duu = 0.f;
 #pragma unroll
-          for (int g = 0; g < NW; ++g) {
-            dd += s_pd[g][cl][sh];
-            duu += s_pu[g][cl][sh];
-          }
-          const float dt = s_dt[cl * PS + s];
-          const float uu = s_u[cl * PS + s];
-          const float dyv = s_dy[cl * PS + s];
-          if constexpr (!EXACT) {  // duu holds Σ_n λ B_n
-            dd = __builtin_fmaf(uu, duu, dd);
-            duu *= dt;
-          }
-          // softplus'(x) = sigmoid(x) = 1 - e^{-Δ}
-          const float dx = p.softplus ? dd * (1.0f - ex2(-dt * kLog2e)) : dd;
-          duu = __builtin_fmaf(Dd, dyv, duu);
-          dD_acc = __builtin_fmaf(dyv, uu, dD_acc);
-          dbias_acc += dx;
-          if (pp < L && dvalid) {
-            const int t = token(pp);
-            store1(static_cast<TIn*>(p.ddelta) + ((int64_t)(b * p.K + k) * L + t) * D + d, dx);
-            if (p.du_part) p.du_part[(((int64_t)k * p.Bsz + b) * L + t) * D + d] = duu;
-            else store1(static_cast<TIn*>(p.du) + ((int64_t)(b * p.Ku + ku) * L + t) * D + d, duu);
-          }
+        for (int g = 0; g < NW; ++g) {
+          dd += s_pd[g][cl][sh];
+          duu += s_pu[g][cl][sh];
         }
+        const float dt = s_dt[cl * PS + s];
+        const float uu = s_u[cl * PS + s];
+        const float dyv = s_dy[cl * PS + s];
+        if constexpr (!EXACT) {  // duu holds Σ_n λ B_n
+          dd = __builtin_fmaf(uu, duu, dd);
+          duu *= dt;
+        }
+        // softplus'(x) = sigmoid(x) = 1 - e^{-Δ}
+        const float dx = p.softplus ? dd * (1.0f - ex2(-dt * kLog2e)) : dd;
+        duu = __builtin_fmaf(Dd, dyv, duu);
+        dD_acc = __builtin_fmaf(dyv * hf, uu, dD_acc);
+        dbias_acc = __builtin_fmaf(dx, hf, dbias_acc);
+        const uint32_t t = (uint32_t)token(min(pp, L - 1));
+        const bool ok = hv && pp < L && dvalid;
+        const uint32_t roff = __umul24(t, rowb) + (uint32_t)dc * ES;
+        const uint32_t roff4 = __umul24(t, (uint32_t)D * 4u) + (uint32_t)dc * 4u;
+        store_out(dx, rs_ddt, ok ? roff : kDrop, 0u, (TIn*)nullptr);
+        store_out(duu, rs_du, ok ? roff : kDrop, 0u, (TIn*)nullptr);
+        buf_store(duu, rs_du32, ok ? roff4 : kDrop, 0u);
       }
       __syncthreads();  // the partial rows are rewritten by the next half
     }
     }  // !AGG
+    if (seg > seg_lo) stage(seg - 1);
   }
 
   if constexpr (AGG) {

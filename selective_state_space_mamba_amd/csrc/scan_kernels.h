@@ -91,9 +91,9 @@ struct ScanParams {
   int ckpt_every;           // positions between checkpoints
   int prio;                 // 1: the scan loop runs at raised wave priority (16-channel blocks)
   int kbase;                // first direction of this launch's grid
-  int fold;                 // 1: the launch's direction (the last, k = K-1) adds the rows of
-                            // directions 0..K-2 from ws_y, in ascending k, to its own output
-                            // and writes the gated result to out (no merge kernel, no row of its own)
+  int fold;                 // 1 (two directions only): the launch's direction, k = 1, adds
+                            // direction 0's row from ws_y to its own output and writes the
+                            // gated result to out (no merge kernel, no row of its own)
 };
 // Template flag EXACT of the kernels below: exact zero-order-hold input term
 // ((e^{ΔA} - 1)/A)·B·u instead of Δ·B·u [MFS §6.2 Step 4, eq (4)].
@@ -199,6 +199,8 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   const auto rs_ws = make_rsrc(p.ws_y ? p.ws_y + ((int64_t)k * p.Bsz + b) * L * D : nullptr,
                                p.ws_y ? (uint32_t)((int64_t)L * D * 4) : 0u);
   const auto rs_out = make_rsrc(direct ? static_cast<TIn*>(p.out) + (int64_t)b * L * D : nullptr, direct ? slice : 0u);
+  // direction 0's fp32 row, read by the folding direction
+  const auto rs_fold = make_rsrc(fold ? p.ws_y + (int64_t)b * L * D : nullptr, fold ? (uint32_t)((int64_t)L * D * 4) : 0u);
   const TIn* __restrict__ B_base = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
   const TIn* __restrict__ C_base = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
   const bool gated = direct && p.z != nullptr;
@@ -321,18 +323,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     }
     if constexpr (!AGG) {
       if (fold) {
-        // the earlier directions' rows at this thread's epilogue positions,
-        // summed in ascending k (read here, a whole tile before their use)
+        // direction 0's row at this thread's epilogue positions (a fold is
+        // planned for two directions only), read here, a whole tile before
+        // its use: one load per position and no wait for it until then
 #pragma unroll
         for (int i = 0; i < TPT; ++i) {
           const uint32_t roff = row_off(p0 + ng * TPT + i, 4u);
-          float acc = 0.f;
-          for (int kk = 0; kk < k; ++kk) {
-            const auto rs = make_rsrc(p.ws_y + ((int64_t)kk * p.Bsz + b) * L * D, (uint32_t)((int64_t)L * D * 4));
-            const float v = buf_load(rs, CB == 64 ? voff_ws : voff_ws + roff, CB == 64 ? roff : 0u, (float*)nullptr);
-            acc = kk == 0 ? v : acc + v;
-          }
-          folded[i] = acc;
+          folded[i] = buf_load(rs_fold, CB == 64 ? voff_ws : voff_ws + roff, CB == 64 ? roff : 0u, (float*)nullptr);
         }
       }
     }
