@@ -536,9 +536,9 @@ def main():
                                dout=douts[i % len(sets)], dir_mode=w.dir_mode, height=w.height, width=w.width,
                                workspace=bws, stream=stream)
         with torch.cuda.stream(stream):
-            for i in range(3):
-                bstep(i)
-            torch.cuda.synchronize()
+            # the inputs above took the host a while, and an idle GPU's clocks
+            # drop: warm up for --warmup-ms of backward work as for the forward
+            bwarm_calls, bwarm_ms = warm_up(torch, stream, bstep, 3, args.warmup_ms)
             _, bwd_ms = timed_region(torch, stream, bstep, args.bwd_steps)
         bwd_s = bwd_ms * 1e-3
         # the training pass with a saved forward state: mamba_scan_fwd_save,
@@ -582,7 +582,7 @@ def main():
                "us_per_call": bwd_s * 1e6, "elements_per_s": el / bwd_s, "bound": "alu",
                "peak_elements_per_s": BWD_ALU_PEAK_ELEM, "frac": el / bwd_s / BWD_ALU_PEAK_ELEM,
                "algorithmic_bytes": bbytes, "hbm_gbs": bbytes / bwd_s / 1e9,
-               "workspace_bytes": int(bws.numel()),
+               "workspace_bytes": int(bws.numel()), "warmup_calls": bwarm_calls, "warmup_gpu_ms": bwarm_ms,
                "saved_state": {"op": "mamba_scan_fwd_save, then mamba_scan_bwd from its saved state (no recompute)",
                                "bytes": int(sbytes), "fwd_save_us_per_call": fsave_s * 1e6,
                                "bwd_us_per_call": bsaved_s * 1e6,
