@@ -420,11 +420,20 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   float carry = 0.f;  // Ā_{p+1}·λ_{p+1}
   if constexpr (!AGG) {
     // the carry into this chunk: fold the later chunks' aggregates
+    // (the aggregates of kFoldBatch chunks loaded together before their updates)
     if (own) {
       const int64_t arow = ((int64_t)k * p.Bsz + b) * (p.nchunks - 1);
-      for (int j = p.nchunks - 1; j > c; --j) {
-        const int64_t r = arow + (j - 1);
-        carry = __builtin_fmaf(ex2(p.agg_dsum[r * D + d] * Al2), carry, p.agg_S[(r * D + d) * N + n]);
+      for (int j0 = p.nchunks - 1; j0 > c; j0 -= kFoldBatch) {
+        float dsv[kFoldBatch], Sv[kFoldBatch];
+#pragma unroll
+        for (int q = 0; q < kFoldBatch; ++q) {
+          const int64_t r = arow + (max(j0 - q, c + 1) - 1);  // (past c + 1: chunk c + 1 again, unused)
+          dsv[q] = p.agg_dsum[r * D + d];
+          Sv[q] = p.agg_S[(r * D + d) * N + n];
+        }
+#pragma unroll
+        for (int q = 0; q < kFoldBatch; ++q)
+          if (j0 - q > c) carry = __builtin_fmaf(ex2(dsv[q] * Al2), carry, Sv[q]);
       }
     }
   }

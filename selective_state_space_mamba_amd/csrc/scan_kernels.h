@@ -48,6 +48,13 @@ namespace mscan {
 #define MSCAN_LDS_PD 0  // 0: the choice above; 1, 2, 3: that depth everywhere
 #endif
 
+// Chunk aggregates whose loads are issued together when a chunk of a time
+// split folds the aggregates of the chunks before it.
+#ifndef MSCAN_FOLD_BATCH
+#define MSCAN_FOLD_BATCH 8
+#endif
+constexpr int kFoldBatch = MSCAN_FOLD_BATCH;
+
 // Traversal kinds: token index of scan position p.
 enum : int { KIND_ROW_FWD = 0, KIND_ROW_REV = 1, KIND_COL_FWD = 2, KIND_COL_REV = 3 };
 
@@ -221,12 +228,27 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       for (int j = 0; j < G; ++j) h[j] = p.init_state[(((int64_t)b * p.K + k) * D + d) * N + ng * G + j];
     }
   } else if (!AGG && dvalid) {
-    // fold the aggregates of chunks 0..c-1: h <- exp(A·ΣΔ_j)·h + S_j, ΣΔ_j kept as ΣΔ'_j
-    for (int jj = 0; jj < c; ++jj) {
-      const float ds = p.agg_dsum[(agg_row + jj) * D + d];
-      const float* S = p.agg_state + ((agg_row + jj) * D + d) * N + ng * G;
+    // fold the aggregates of chunks 0..c-1: h <- exp(A·ΣΔ_j)·h + S_j, ΣΔ_j kept as ΣΔ'_j.
+    // The aggregates of kFoldBatch chunks are loaded together before their
+    // updates, so chunk c waits for ceil(c / kFoldBatch) memory round trips
+    // instead of c (the loads do not depend on h; only the updates chain).
+    for (int j0 = 0; j0 < c; j0 += kFoldBatch) {
+      float dsv[kFoldBatch], Sv[kFoldBatch][G];
 #pragma unroll
-      for (int j = 0; j < G; ++j) h[j] = __builtin_fmaf(ex2(ds * Al2[j]), h[j], S[j]);
+      for (int q = 0; q < kFoldBatch; ++q) {
+        const int jj = min(j0 + q, c - 1);  // (past c: the last aggregate again, unused)
+        dsv[q] = p.agg_dsum[(agg_row + jj) * D + d];
+        const float* S = p.agg_state + ((agg_row + jj) * D + d) * N + ng * G;
+#pragma unroll
+        for (int j = 0; j < G; ++j) Sv[q][j] = S[j];
+      }
+#pragma unroll
+      for (int q = 0; q < kFoldBatch; ++q) {
+        if (j0 + q < c) {
+#pragma unroll
+          for (int j = 0; j < G; ++j) h[j] = __builtin_fmaf(ex2(dsv[q] * Al2[j]), h[j], Sv[q][j]);
+        }
+      }
     }
   }
   const float bias = (dvalid && p.delta_bias) ? p.delta_bias[k * D + d] : 0.f;

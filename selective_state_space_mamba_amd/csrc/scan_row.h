@@ -201,13 +201,29 @@ __global__ void __launch_bounds__(64) scan_row_kernel(const ScanParams p) {
         if (FULL || n < N) h[n] = p.init_state[(((int64_t)b * p.K + k) * D + dc) * N + n];
     }
   } else if (!AGG) {
-    // fold the aggregates of chunks 0..c-1: h <- 2^(ΣΔ'_j·A)·h + S_j
-    for (int jj = 0; jj < c; ++jj) {
-      const float ds = p.agg_dsum[(agg_row + jj) * D + dc];
-      const float* S = p.agg_state + ((agg_row + jj) * D + dc) * N;
+    // fold the aggregates of chunks 0..c-1: h <- 2^(ΣΔ'_j·A)·h + S_j, the
+    // aggregates of FB chunks loaded together before their updates (about
+    // 64 registers of them), so chunk c waits for ceil(c / FB) memory round
+    // trips instead of c
+    constexpr int FB = NP >= 64 ? 1 : 64 / NP < kFoldBatch ? 64 / NP : kFoldBatch;
+    for (int j0 = 0; j0 < c; j0 += FB) {
+      float dsv[FB], Sv[FB][NP];
 #pragma unroll
-      for (int n = 0; n < NP; ++n)
-        if (FULL || n < N) h[n] = __builtin_fmaf(ex2(ds * Al2[n]), h[n], S[n]);
+      for (int q = 0; q < FB; ++q) {
+        const int jj = min(j0 + q, c - 1);  // (past c: the last aggregate again, unused)
+        dsv[q] = p.agg_dsum[(agg_row + jj) * D + dc];
+        const float* S = p.agg_state + ((agg_row + jj) * D + dc) * N;
+#pragma unroll
+        for (int n = 0; n < NP; ++n) Sv[q][n] = (FULL || n < N) ? S[n] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < FB; ++q) {
+        if (j0 + q < c) {
+#pragma unroll
+          for (int n = 0; n < NP; ++n)
+            if (FULL || n < N) h[n] = __builtin_fmaf(ex2(dsv[q] * Al2[n]), h[n], Sv[q][n]);
+        }
+      }
     }
   }
   const float bias = p.delta_bias ? p.delta_bias[k * D + dc] : 0.f;
