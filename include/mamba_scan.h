@@ -55,8 +55,8 @@ typedef enum {
   MAMBA_OK = 0,
   MAMBA_ERR_INVALID = -1,     /* NULL required pointer, size <= 0, L != H*W, unknown mode or dtype */
   MAMBA_ERR_UNSUPPORTED = -2, /* valid but not built: N above 64 (for the backward and
-                                 mamba_scan_fwd_save, N above 32 or dim not a multiple of
-                                 8), dim not a multiple of 8 (bf16) or 4 (f32), a pointer
+                                 mamba_scan_fwd_save also dim not a multiple of 8), dim
+                                 not a multiple of 8 (bf16) or 4 (f32), a pointer
                                  not 16-byte aligned, or sizes beyond
                                  the 32-bit offsets used inside one (batch, direction) slice:
                                  (seqlen+64)*dim*sizeof(dtype) below 2^31 bytes, and for
@@ -96,7 +96,7 @@ typedef struct {
   int64_t batch;   /* B >= 1 */
   int64_t dim;     /* D >= 1, the channel count (d_inner); a multiple of 8 for bf16, of 4 for f32 */
   int64_t seqlen;  /* L >= 1 tokens (ignored by mamba_scan_step) */
-  int64_t dstate;  /* N, state size per channel: 1..64 (the backward: 1..32) */
+  int64_t dstate;  /* N, state size per channel: 1..64 */
   int64_t height;  /* MAMBA_DIR_CROSS2D only: grid rows H, with H*W == L; else 0 */
   int64_t width;   /* MAMBA_DIR_CROSS2D only: grid columns W; else 0 */
   int32_t dtype;          /* mamba_dtype */
@@ -218,7 +218,7 @@ MAMBA_API size_t mamba_scan_bwd_workspace_bytes(const mamba_dims* dims, int dir_
 /*
  * Bytes of the saved forward state that mamba_scan_fwd_save writes and
  * mamba_scan_bwd can read in place of its forward recompute: the state before
- * every 16th position (every 32nd when N is above 16), [K][B][ceil(L/16 or
+ * every 16th position (every 32nd when N is 17..32), [K][B][ceil(L/16 or
  * 32)][D][N] float32, and, when gated is
  * nonzero (a scan with z whose dz will be asked for), after it (at a 256-byte
  * aligned offset) the ungated per-direction outputs [K][B][L][D] float32.
@@ -237,7 +237,7 @@ MAMBA_API size_t mamba_scan_saved_bytes(const mamba_dims* dims, int dir_mode, in
  * arguments.  Same errors as mamba_scan_fwd, plus MAMBA_ERR_INVALID for a
  * NULL saved and MAMBA_ERR_WORKSPACE when saved_bytes is below
  * mamba_scan_saved_bytes(dims, dir_mode, z != NULL); built for dstate N in
- * 1..32 and a channel count that is a multiple of 8, like the backward pass.
+ * 1..64 and a channel count that is a multiple of 8, like the backward pass.
  */
 MAMBA_API int mamba_scan_fwd_save(const void* u, const void* delta, const float* A, const void* B, const void* C,
                                   const float* D, const void* z, const float* delta_bias, const mamba_dims* dims,
@@ -266,9 +266,11 @@ MAMBA_API int mamba_scan_fwd_save(const void* u, const void* delta, const float*
  *   dA = Σ λ·(Δ·Ā·h_prev + (∂c/∂A)·B·u),  dB = Σ_d λ·c·u,  dC = Σ_d dy·h,
  *   dD = Σ dy·u,  dz = dout·(Σ_k y_k)·silu'(z),  ddelta = dΔ·sigmoid(delta + bias)
  * (c = Δ, or (Ā - 1)/A with exact_zoh).  The gradient outputs must not alias
- * any input or each other.  Built for dstate N in 1..32 and a channel count
+ * any input or each other.  Built for dstate N in 1..64 and a channel count
  * that is a multiple of 8; other N and channel counts give
- * MAMBA_ERR_UNSUPPORTED.  dims->workspace must hold
+ * MAMBA_ERR_UNSUPPORTED (above 32 states the states are taken in groups of
+ * 16, each group's share of du and ddelta summed in float32 before the
+ * conversion to dtype).  dims->workspace must hold
  * mamba_scan_bwd_workspace_bytes() bytes; its contents need not be
  * initialised.  saved: NULL to recompute the forward states, or the buffer
  * mamba_scan_fwd_save wrote for these same inputs, dims and dir_mode (read

@@ -205,19 +205,21 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 constexpr int kBwdBlock = 16;     // channels per workgroup of scan_bwd_kernel
 constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per CU; 1 at N = 32)
 constexpr int kBwdMinChunk = 1024;  // shortest time chunk of a split adjoint
+constexpr int kBwdGroup = 16;     // states per group above 32 states
 struct BwdPlan {
   Plan fwd;
-  int nblk, ntiles, every, nchunks, chunk_len;
-  size_t agg, ws_y, ckpt, dB, dC, du, dA, dD, dbias, bagg_S, bagg_dsum, total;
+  int nblk, ntiles, every, nchunks, chunk_len, ngroups;
+  size_t agg, ws_y, ckpt, dB, dC, du, ddelta, dA, dD, dbias, bagg_S, bagg_dsum, total;
 };
 
 int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const int rc = make_plan(g, mode, &bp->fwd);
   if (rc != MAMBA_OK) return rc;
   // one state per thread (16 channels x N states per workgroup, N rounded up
-  // to a power of two, at most 512 threads) and checkpoints at multiples of
-  // the tile
-  if (g->dstate > 32 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
+  // to a power of two, at most 512 threads; above 32 states, groups of 16
+  // states in workgroups of their own) and checkpoints at multiples of the
+  // tile
+  if (g->dstate > 64 || kTile != 32) return MAMBA_ERR_UNSUPPORTED;
   // the per-element kernels of the backward (dz of several directions, the
   // sums) take 8 consecutive channels per thread
   if (g->dim % 8 != 0) return MAMBA_ERR_UNSUPPORTED;
@@ -226,14 +228,18 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   const Plan& pl = bp->fwd;
   const int64_t K = pl.K, Bz = g->batch, L = g->seqlen, Dm = g->dim, N = g->dstate;
   bp->nblk = (int)((Dm + kBwdBlock - 1) / kBwdBlock);
-  // checkpoint interval = the adjoint's segment: 16 positions, 32 above 16
+  // state groups: above 32 states, workgroups of 16 states each (the sums over
+  // states of a channel's gradients are then summed over the groups)
+  const int64_t G = N > 32 ? (N + kBwdGroup - 1) / kBwdGroup : 1;
+  bp->ngroups = (int)G;
+  // checkpoint interval = the adjoint's segment: 16 positions, 32 for 17..32
   // states (the adjoint kernel's segment for 32 thread rows)
-  bp->every = N > 16 ? 32 : 16;
+  bp->every = (N > 16 && G == 1) ? 32 : 16;
   bp->ntiles = (int)((L + bp->every - 1) / bp->every);
   // Time split of the adjoint when its rows fill less than one round of
   // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
-  const int64_t rows = (int64_t)bp->nblk * Bz * K;
-  const int64_t slots = N > 16 ? kBwdSlots / 2 : kBwdSlots;
+  const int64_t rows = (int64_t)bp->nblk * Bz * K * G;
+  const int64_t slots = (N > 16 && G == 1) ? kBwdSlots / 2 : kBwdSlots;
   int64_t nch = 1;
   if (rows < slots) {
     nch = (2 * slots + rows - 1) / rows;
@@ -260,10 +266,13 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   bp->ckpt = take((size_t)K * Bz * bp->ntiles * Dm * N * f4);
   bp->dB = take((size_t)bp->nblk * Bz * K * L * N * f4);
   bp->dC = take((size_t)bp->nblk * Bz * K * L * N * f4);
-  bp->du = pl.Ku != K ? take((size_t)K * Bz * L * Dm * f4) : off;
+  // du and ddelta in fp32 parts: du of the cross scan per direction (its u is
+  // shared), both per state group with groups
+  bp->du = (pl.Ku != K || G > 1) ? take((size_t)G * K * Bz * L * Dm * f4) : off;
+  bp->ddelta = G > 1 ? take((size_t)G * K * Bz * L * Dm * f4) : off;
   bp->dA = take((size_t)nch * Bz * K * Dm * N * f4);
-  bp->dD = take((size_t)nch * Bz * K * Dm * f4);
-  bp->dbias = take((size_t)nch * Bz * K * Dm * f4);
+  bp->dD = take((size_t)G * nch * Bz * K * Dm * f4);
+  bp->dbias = take((size_t)G * nch * Bz * K * Dm * f4);
   bp->bagg_S = take((size_t)K * Bz * (nch - 1) * Dm * N * f4);
   bp->bagg_dsum = take((size_t)K * Bz * (nch - 1) * Dm * f4);
   bp->total = off;
@@ -370,7 +379,7 @@ int dispatch_fwd(const mamba_dims* dims, const ScanParams& p, const Plan& pl, hi
 }
 
 // Saved forward state (mamba_scan_fwd_save -> mamba_scan_bwd): the state
-// before every 16th position (32nd above 16 states), [K][B][ntiles][D][N] fp32, then, for a
+// before every 16th position (32nd at 17..32 states), [K][B][ntiles][D][N] fp32, then, for a
 // gated scan, the ungated per-direction rows [K][B][L][D] fp32 (dz needs them).
 struct SavedLayout {
   BwdPlan bp;
@@ -606,9 +615,12 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
   q.dz = dz_here ? dz : nullptr;
   q.dz_here = dz_here ? 1 : 0;
   const bool shared_u = pl.Ku != pl.K;
-  q.du = shared_u ? nullptr : du;
-  q.du_part = shared_u ? wsf(bp.du) : nullptr;
+  const bool groups = bp.ngroups > 1;
+  q.du = (shared_u || groups) ? nullptr : du;
+  q.du_part = (shared_u || groups) ? wsf(bp.du) : nullptr;
   q.ddelta = ddelta;
+  q.ddelta_part = groups ? wsf(bp.ddelta) : nullptr;
+  q.ngroups = bp.ngroups;
   q.dB_part = wsf(bp.dB);
   q.dC_part = wsf(bp.dC);
   q.dA_part = wsf(bp.dA);
@@ -635,26 +647,32 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A, const void*
             : (exact ? dispatch_bwd_f32_exact(N, q, stream) : dispatch_bwd_f32_simple(N, q, stream));
   if (rc != MAMBA_OK) return rc;
 
-  // 4. sums over channel blocks (dB, dC), directions (du of the cross scan)
-  // and batches (dA, dD, ddelta_bias)
-  const int64_t K = pl.K, Bz = dims->batch, Dm = dims->dim;
+  // 4. sums over channel blocks (dB, dC), directions (du of the cross scan),
+  // state groups (du, ddelta) and batches (dA, dD, ddelta_bias)
+  const int64_t K = pl.K, Bz = dims->batch, Dm = dims->dim, G = bp.ngroups;
   const int64_t nbc = Bz * K * dims->seqlen * N;
+  // du parts: [G][K] slices of [B][L][D] (shared u) or [G] slices of [B][K][L][D]
+  const int64_t du_sl = shared_u ? G * K : G, du_n = shared_u ? nrow : nrow * K;
   if (bf16) {
     rc = launch_bwd_sum<uint16_t>(q.dB_part, bp.nblk, nbc, nbc, dB, stream, q.dC_part, dC);
-    if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<uint16_t>(q.du_part, K, nrow, nrow, du, stream);
+    if (rc == MAMBA_OK && (shared_u || groups)) rc = launch_bwd_sum<uint16_t>(q.du_part, du_sl, du_n, du_n, du, stream);
+    if (rc == MAMBA_OK && groups) rc = launch_bwd_sum<uint16_t>(q.ddelta_part, G, nrow * K, nrow * K, ddelta, stream);
   } else {
     rc = launch_bwd_sum<float>(q.dB_part, bp.nblk, nbc, nbc, dB, stream, q.dC_part, dC);
-    if (rc == MAMBA_OK && shared_u) rc = launch_bwd_sum<float>(q.du_part, K, nrow, nrow, du, stream);
+    if (rc == MAMBA_OK && (shared_u || groups)) rc = launch_bwd_sum<float>(q.du_part, du_sl, du_n, du_n, du, stream);
+    if (rc == MAMBA_OK && groups) rc = launch_bwd_sum<float>(q.ddelta_part, G, nrow * K, nrow * K, ddelta, stream);
   }
-  // (the dA, dD, ddelta_bias parts are [chunk][batch][K][...]: one slice per (chunk, batch))
+  // (the dA parts are [chunk][batch][K][...]: one slice per (chunk, batch); the
+  // dD and ddelta_bias parts [group][chunk][batch][K][...])
   const int64_t nsl = (int64_t)bp.nchunks * Bz;
+  const int64_t nsl_g = G * nsl;
   if (rc == MAMBA_OK) rc = launch_bwd_sum<float>(q.dA_part, nsl, K * Dm * N, K * Dm * N, dA, stream);
   if (rc == MAMBA_OK && dD && ddelta_bias)
-    rc = launch_bwd_sum<float>(q.dD_part, nsl, K * Dm, K * Dm, dD, stream, q.dbias_part, ddelta_bias);
+    rc = launch_bwd_sum<float>(q.dD_part, nsl_g, K * Dm, K * Dm, dD, stream, q.dbias_part, ddelta_bias);
   else if (rc == MAMBA_OK && dD)
-    rc = launch_bwd_sum<float>(q.dD_part, nsl, K * Dm, K * Dm, dD, stream);
+    rc = launch_bwd_sum<float>(q.dD_part, nsl_g, K * Dm, K * Dm, dD, stream);
   else if (rc == MAMBA_OK && ddelta_bias)
-    rc = launch_bwd_sum<float>(q.dbias_part, nsl, K * Dm, K * Dm, ddelta_bias, stream);
+    rc = launch_bwd_sum<float>(q.dbias_part, nsl_g, K * Dm, K * Dm, ddelta_bias, stream);
   return rc;
 }
 

@@ -18,15 +18,18 @@
 // With the simplified rule (B̄ = Δ·B) the channel's u and Δ factor out of the
 // state sums: dΔ_p = Σ_n λ h_{p-1} A Ā + u·Σ_n λ B_n and du = Δ·Σ_n λ B_n + D·dy,
 // so the per-state terms are λ h_{p-1} Ā A_n and λ B_n (and Δ·u is staged once).
-// The forward pass with state checkpoints every 16 positions (32 above 16
+// The forward pass with state checkpoints every 16 positions (32 at 17..32
 // states) runs first
 // (scan_chunk_kernel with ScanParams::ckpt); scan_bwd_kernel then walks each
 // (direction, batch, 16-channel block) backwards one segment (16 positions,
-// 32 for N above 16) at a time: it recomputes the segment's states from its
+// 32 for N = 17..32) at a time: it recomputes the segment's states from its
 // checkpoint into registers, then runs the adjoint recurrence over its
 // 16-position halves.  Sums over states go through LDS (like the forward readout); sums
 // over the block's 16 channels (dB, dC) through a register butterfly across
-// each 16-lane row; sums over blocks and batches in bwd_sum_kernel.
+// each 16-lane row; sums over blocks and batches in bwd_sum_kernel.  Above 32
+// states the states are split into groups of 16, one workgroup each; their
+// shares of the per-channel sums (du, ddelta, ddelta_bias) are added in
+// bwd_sum_kernel.
 #pragma once
 
 #include "scan_kernels.h"
@@ -91,21 +94,30 @@ struct BwdParams {
   void* dz;                 // [Bsz][L][Dm]: written while staging when dz_here
   int dz_here;              // one direction and a gate: dz from this direction's row
   void* du;                 // [Bsz][Ku][L][Dm] (Ku = K), or null when du_part is used
-  float* du_part;           // [K][Bsz][L][Dm] (the cross scan shares u), or null
+  float* du_part;           // [ngroups][K][Bsz][L][Dm] (the cross scan shares u) or
+                            // [ngroups][Bsz][K][L][Dm] (groups, u per direction), or null
   void* ddelta;             // [Bsz][K][L][Dm]
   float* dB_part;           // [nblk_d][Bsz][K][L][N]
   float* dC_part;           // [nblk_d][Bsz][K][L][N]
   float* dA_part;           // [nchunks][Bsz][K][Dm][N]
-  float* dD_part;           // [nchunks][Bsz][K][Dm]
-  float* dbias_part;        // [nchunks][Bsz][K][Dm]
+  float* dD_part;           // [ngroups][nchunks][Bsz][K][Dm] (zero past group 0)
+  float* dbias_part;        // [ngroups][nchunks][Bsz][K][Dm]
   float* dinit;             // [Bsz][K][Dm][N] or null
+  // State groups (N above 32): the grid holds ngroups workgroups per (channel
+  // block, chunk, batch, direction), group g taking states 16g .. 16g+15 (the
+  // last may hold fewer); the sums over states of a channel's gradients are
+  // then partial per group: ddelta and du go as fp32 parts to ddelta_part and
+  // du_part, dbias as parts per group, and D·dy, dD and dz come from group 0.
+  float* ddelta_part;       // [ngroups][Bsz][K][L][Dm] with ngroups > 1, else null
   // time split: the adjoint of chunk c starts from the carry of chunks c+1..
   float* agg_S;             // [K][Bsz][nchunks-1][Dm][N]: carry out of chunk j >= 1 from a zero carry in
   float* agg_dsum;          // [K][Bsz][nchunks-1][Dm]: ΣΔ over chunk j
   int nchunks, chunk_len;   // chunks per sequence (chunk_len a multiple of 32)
   int chunk0, grid_chunks;  // chunks chunk0 .. chunk0+grid_chunks-1 are this launch's
   int Bsz, Dm, L, H, W, K, Ku, kinds, nblk_d, ntiles, softplus;
-  int N;                    // state size (the kernel may run a larger power-of-two instantiation)
+  int N;                    // state size (the kernel may run a larger power-of-two instantiation,
+                            // or groups of NP states)
+  int ngroups;              // state groups (1: all N states in one workgroup)
 };
 
 // dz = dout·y_all·silu'(z), y_all = Σ_k y_k (ungated), silu'(z) = σ(z)·(1 + z·(1 - σ(z))),
@@ -235,7 +247,10 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
 // NP: the instantiation's power-of-two state count; FULL: N == NP (N a
 // compile-time constant), else N = p.N < NP and the thread rows n >= N hold
 // no state (as the rows past N do for N < 4).
-template <typename TIn, int NP, bool FULL, bool EXACT, bool AGG>
+//
+// GRP: a state group of a larger N (p.ngroups groups of NP states; the row
+// stride of A, B, C, the checkpoints and the per-state gradients is p.N).
+template <typename TIn, int NP, bool FULL, bool EXACT, bool AGG, bool GRP = false>
 __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVES_EXACT : MSCAN_BWD_WAVES)
     scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
@@ -254,7 +269,15 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   constexpr int QI = (NP * TS + NT - 1) / NT;  // B (and C) elements staged per thread per segment (at most)
   static_assert(TS % NGP == 0 && TH % 4 == 0, "segment splits over the thread rows");
   static_assert(NP <= 32, "one state per thread, at most 512 threads");
-  const int N = FULL ? NP : p.N;
+  static_assert(!GRP || !FULL, "a group's state count is read at run time");
+  // grid: (group,) channel block, chunk, batch, direction
+  const int nblocks = gridDim.x;
+  int bid = logical_block(blockIdx.x, nblocks, 4);
+  const int gi = GRP ? bid % p.ngroups : 0;  // state group
+  if (GRP) bid /= p.ngroups;
+  const int n0 = GRP ? gi * NP : 0;           // its first state
+  const int NS = GRP ? p.N : (FULL ? NP : p.N);  // states per row of A, B, C, checkpoints, per-state gradients
+  const int N = GRP ? min(NP, p.N - n0) : NS;    // states of this workgroup
   constexpr bool KEEP_ABAR = MSCAN_BWD_KEEP_ABAR;
 
   __shared__ __attribute__((aligned(16))) float s_dt[CB * PS];   // Δ
@@ -280,8 +303,6 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   const uint32_t m1 = (cl & 2) ? ~0u : 0u, m0 = (cl & 1) ? ~0u : 0u;
   const float nvf = nvalid ? 1.f : 0.f;  // rows past N add nothing to the state sums
 
-  const int nblocks = gridDim.x;
-  int bid = logical_block(blockIdx.x, nblocks, 4);
   const int dblk = bid % p.nblk_d;
   bid /= p.nblk_d;
   const int c = p.chunk0 + bid % p.grid_chunks;
@@ -306,8 +327,8 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
 
   const TIn* u_s = static_cast<const TIn*>(p.u) + (int64_t)(b * p.Ku + ku) * L * D;
   const TIn* dl_s = static_cast<const TIn*>(p.delta) + (int64_t)(b * p.K + k) * L * D;
-  const TIn* B_s = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * N;
-  const TIn* C_s = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * N;
+  const TIn* B_s = static_cast<const TIn*>(p.B) + (int64_t)(b * p.K + k) * L * NS + n0;
+  const TIn* C_s = static_cast<const TIn*>(p.C) + (int64_t)(b * p.K + k) * L * NS + n0;
   const TIn* go_s = static_cast<const TIn*>(p.dout) + (int64_t)b * L * D;
   const bool gated = p.z != nullptr;
   const TIn* z_s = gated ? static_cast<const TIn*>(p.z) + (int64_t)b * L * D : go_s;  // (no gate: unused loads)
@@ -315,9 +336,9 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   // element 0 (one cache line, unused; of dout when there are no rows)
   const float* y_s = p.ws_y ? p.ws_y + ((int64_t)k * p.Bsz + b) * L * D : static_cast<const float*>(p.dout);
   const int64_t y_mask = p.dz_here ? ~(int64_t)0 : 0;
-  const float* ck_s = p.ckpt + ((int64_t)k * p.Bsz + b) * p.ntiles * D * N;
+  const float* ck_s = p.ckpt + ((int64_t)k * p.Bsz + b) * p.ntiles * D * NS;
   const bool own = nvalid && dvalid;  // this thread's (channel, state) exists
-  const int64_t ck_off = own ? (int64_t)d * N + n : 0;
+  const int64_t ck_off = own ? (int64_t)d * NS + n0 + n : 0;
 
   // Stores inside the segment loop go through buffer descriptors over this
   // workgroup's slices (each at most 2^31 bytes: the plan's limits), every
@@ -331,22 +352,28 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   const uint32_t rowb = (uint32_t)D * ES;  // bytes per token row
   const uint32_t slice = (uint32_t)((int64_t)L * D * ES);
   const bool du32 = p.du_part != nullptr;
-  const auto rs_dz = make_rsrc(p.dz_here ? static_cast<TIn*>(p.dz) + (int64_t)b * L * D : nullptr,
-                               p.dz_here ? slice : 0u);
-  const auto rs_ddt = make_rsrc(static_cast<TIn*>(p.ddelta) + (int64_t)(b * p.K + k) * L * D, slice);
+  const bool dz_here = p.dz_here && gi == 0;  // (dz: the same from every group)
+  const auto rs_dz = make_rsrc(dz_here ? static_cast<TIn*>(p.dz) + (int64_t)b * L * D : nullptr,
+                               dz_here ? slice : 0u);
+  const auto rs_ddt = make_rsrc(GRP ? nullptr : static_cast<TIn*>(p.ddelta) + (int64_t)(b * p.K + k) * L * D,
+                                GRP ? 0u : slice);
+  // (groups: the fp32 parts of ddelta)
+  const auto rs_ddt32 = make_rsrc(GRP ? p.ddelta_part + (((int64_t)gi * p.Bsz + b) * p.K + k) * L * D : nullptr,
+                                  GRP ? (uint32_t)((int64_t)L * D * 4) : 0u);
   const auto rs_du = make_rsrc(du32 ? nullptr : static_cast<TIn*>(p.du) + (int64_t)(b * p.Ku + ku) * L * D,
                                du32 ? 0u : slice);
-  const auto rs_du32 = make_rsrc(du32 ? p.du_part + ((int64_t)k * p.Bsz + b) * L * D : nullptr,
+  const int64_t du_row = p.Ku != p.K ? ((int64_t)gi * p.K + k) * p.Bsz + b : ((int64_t)gi * p.Bsz + b) * p.K + k;
+  const auto rs_du32 = make_rsrc(du32 ? p.du_part + du_row * L * D : nullptr,
                                  du32 ? (uint32_t)((int64_t)L * D * 4) : 0u);
-  const int64_t bc_slice = (((int64_t)dblk * p.Bsz + b) * p.K + k) * L * N;
-  const auto rs_dB = make_rsrc(p.dB_part + bc_slice, (uint32_t)((int64_t)L * N * 4));
-  const auto rs_dC = make_rsrc(p.dC_part + bc_slice, (uint32_t)((int64_t)L * N * 4));
+  const int64_t bc_slice = (((int64_t)dblk * p.Bsz + b) * p.K + k) * L * NS;
+  const auto rs_dB = make_rsrc(p.dB_part + bc_slice, (uint32_t)((int64_t)L * NS * 4));
+  const auto rs_dC = make_rsrc(p.dC_part + bc_slice, (uint32_t)((int64_t)L * NS * 4));
 
-  const float Anat = own ? p.A[((int64_t)k * D + d) * N + n] : 0.f;
+  const float Anat = own ? p.A[((int64_t)k * D + d) * NS + n0 + n] : 0.f;
   const float Al2 = Anat * kLog2e;  // e^{ΔA} = 2^{Δ·A·log2 e}
   const float invA = Anat != 0.f ? 1.0f / Anat : 0.f;
   const float bias = (dvalid && p.delta_bias) ? p.delta_bias[k * D + d] : 0.f;
-  const float Dd = (dvalid && p.D) ? p.D[k * D + d] : 0.f;
+  const float Dd = (dvalid && p.D && gi == 0) ? p.D[k * D + d] : 0.f;  // (D·dy: group 0's du part)
 
   // raw global values of one segment (rows clamped into the sequence; padded
   // rows are zeroed at staging)
@@ -370,11 +397,11 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
       const int q = min(tid + i * NT, N * TS - 1);
-      const int64_t off = (int64_t)token(min(p0 + q / N, L - 1)) * N + q % N;
+      const int64_t off = (int64_t)token(min(p0 + q / N, L - 1)) * NS + q % N;
       if constexpr (!AGG) r.B[i] = B_s[off];
       r.C[i] = C_s[off];
     }
-    if constexpr (!AGG) r.h0 = ck_s[(int64_t)seg * D * N + ck_off];
+    if constexpr (!AGG) r.h0 = ck_s[(int64_t)seg * D * NS + ck_off];
   };
   auto stage_seg = [&](int seg, const Raw& r) __attribute__((always_inline)) {
     const int p0 = seg * TS;
@@ -429,7 +456,7 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
         for (int q = 0; q < kFoldBatch; ++q) {
           const int64_t r = arow + (max(j0 - q, c + 1) - 1);  // (past c + 1: chunk c + 1 again, unused)
           dsv[q] = p.agg_dsum[r * D + d];
-          Sv[q] = p.agg_S[(r * D + d) * N + n];
+          Sv[q] = p.agg_S[(r * D + d) * NS + n0 + n];
         }
 #pragma unroll
         for (int q = 0; q < kFoldBatch; ++q)
@@ -555,7 +582,7 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
         // cl, lane cl >= 8 with dC of step cl - 8
         const float sBC = row_sum_transpose16(pBC, m1, m0);
         const int pp = p0 + half * TH + qt * 8 + (cl & 7);
-        const uint32_t off = __umul24((uint32_t)token(min(pp, L - 1)), (uint32_t)N * 4u) + (uint32_t)n * 4u;
+        const uint32_t off = __umul24((uint32_t)token(min(pp, L - 1)), (uint32_t)NS * 4u) + (uint32_t)(n0 + n) * 4u;
         const bool ok = nvalid && pp < L;
         buf_store(sBC, rs_dB, (ok && cl < 8) ? off : kDrop, 0u);
         buf_store(sBC, rs_dC, (ok && cl >= 8) ? off : kDrop, 0u);
@@ -596,7 +623,10 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
         const bool ok = hv && pp < L && dvalid;
         const uint32_t roff = __umul24(t, rowb) + (uint32_t)dc * ES;
         const uint32_t roff4 = __umul24(t, (uint32_t)D * 4u) + (uint32_t)dc * 4u;
-        store_out(dx, rs_ddt, ok ? roff : kDrop, 0u, (TIn*)nullptr);
+        if constexpr (GRP)
+          buf_store(dx, rs_ddt32, ok ? roff4 : kDrop, 0u);
+        else
+          store_out(dx, rs_ddt, ok ? roff : kDrop, 0u, (TIn*)nullptr);
         store_out(duu, rs_du, ok ? roff : kDrop, 0u, (TIn*)nullptr);
         buf_store(duu, rs_du32, ok ? roff4 : kDrop, 0u);
       }
@@ -609,8 +639,8 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   if constexpr (AGG) {
     if (dvalid) {
       const int64_t r = ((int64_t)k * p.Bsz + b) * (p.nchunks - 1) + (c - 1);
-      if (nvalid) p.agg_S[(r * D + d) * N + n] = carry;
-      if (ng == 0) p.agg_dsum[r * D + d] = dsum;
+      if (nvalid) p.agg_S[(r * D + d) * NS + n0 + n] = carry;
+      if (ng == 0 && gi == 0) p.agg_dsum[r * D + d] = dsum;
     }
     return;
   }
@@ -622,8 +652,8 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
   __syncthreads();
   if (dvalid) {
     if (nvalid) {
-      const int64_t o = (((int64_t)b * p.K + k) * D + d) * N + n;
-      p.dA_part[(int64_t)c * p.Bsz * p.K * D * N + o] = dA_acc;
+      const int64_t o = (((int64_t)b * p.K + k) * D + d) * NS + n0 + n;
+      p.dA_part[(int64_t)c * p.Bsz * p.K * D * NS + o] = dA_acc;
       if (p.dinit && c == 0) p.dinit[o] = carry;
     }
     if (ng == 0) {
@@ -633,8 +663,8 @@ __global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVE
         sD += s_red[g * CB + cl];
         sb += s_red[(NGP + g) * CB + cl];
       }
-      const int64_t o = (((int64_t)c * p.Bsz + b) * p.K + k) * D + d;
-      p.dD_part[o] = sD;
+      const int64_t o = ((((int64_t)gi * p.nchunks + c) * p.Bsz + b) * p.K + k) * D + d;
+      p.dD_part[o] = gi == 0 ? sD : 0.f;  // (dD: the same sum in every group)
       p.dbias_part[o] = sb;
     }
   }

@@ -220,9 +220,29 @@ int launch_bwd_np(const BwdParams& p, hipStream_t s) {
   else return p.N == NP ? launch_bwd<TIn, NP, true, EXACT>(p, s) : launch_bwd<TIn, NP, false, EXACT>(p, s);
 }
 
+// Above 32 states: p.ngroups workgroups of 16 states per (channel block,
+// chunk, batch, direction), the group the fastest-varying grid index.
+template <typename TIn, bool EXACT>
+int launch_bwd_groups(BwdParams p, hipStream_t stream) {
+  constexpr int NP = 16, NT = 16 * NP;
+  if (p.nchunks > 1) {  // aggregate pass over chunks 1..
+    p.chunk0 = 1;
+    p.grid_chunks = p.nchunks - 1;
+    const unsigned blocks = (unsigned)((int64_t)p.nblk_d * p.grid_chunks * p.Bsz * p.K * p.ngroups);
+    hipLaunchKernelGGL((scan_bwd_kernel<TIn, NP, false, false, true, true>), dim3(blocks), dim3(NT), 0, stream, p);
+    if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
+  }
+  p.chunk0 = 0;
+  p.grid_chunks = p.nchunks;
+  const unsigned blocks = (unsigned)((int64_t)p.nblk_d * p.grid_chunks * p.Bsz * p.K * p.ngroups);
+  hipLaunchKernelGGL((scan_bwd_kernel<TIn, NP, false, EXACT, false, true>), dim3(blocks), dim3(NT), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
+}
+
 template <typename TIn, bool EXACT>
 int dispatch_bwd(int64_t N, const BwdParams& p, hipStream_t s) {
-  if (N < 1 || N > 32) return MAMBA_ERR_UNSUPPORTED;
+  if (N < 1 || N > 64) return MAMBA_ERR_UNSUPPORTED;
+  if (N > 32) return p.ngroups == (N + 15) / 16 ? launch_bwd_groups<TIn, EXACT>(p, s) : MAMBA_ERR_UNSUPPORTED;
   if (N <= 1) return launch_bwd_np<TIn, 1, EXACT>(p, s);
   if (N <= 2) return launch_bwd_np<TIn, 2, EXACT>(p, s);
   if (N <= 4) return launch_bwd_np<TIn, 4, EXACT>(p, s);

@@ -157,8 +157,12 @@ def test_bwd_workspace_and_validation(lib):
     cross = ms.bwd_workspace_bytes(dims(seqlen=96, height=8, width=12), ms.DIR_CROSS2D)
     assert cross >= 4 * 4 * Bz * 96 * Dm * 2  # per-direction rows and per-direction du
     assert ms.bwd_workspace_bytes(dims(dstate=32), ms.DIR_FWD) > need  # N = 32 is built
-    assert ms.bwd_workspace_bytes(dims(dstate=12), ms.DIR_FWD) > 0  # any N up to 32
-    for bad in (dims(dstate=64), dims(dstate=33), dims(seqlen=0), dims(dim=60), dims(dim=36, dtype=ms.DTYPE_F32)):
+    assert ms.bwd_workspace_bytes(dims(dstate=12), ms.DIR_FWD) > 0  # any N up to 64
+    # above 32 states: groups of 16 states, with fp32 parts of du and ddelta per group
+    n64 = ms.bwd_workspace_bytes(dims(dstate=64), ms.DIR_FWD)
+    assert n64 >= 4 * (2 * 4 * Bz * L * Dm + 2 * (Dm // 16) * Bz * L * 64)
+    assert ms.bwd_workspace_bytes(dims(dstate=33), ms.DIR_FWD) > 0
+    for bad in (dims(dstate=65), dims(seqlen=0), dims(dim=60), dims(dim=36, dtype=ms.DTYPE_F32)):
         with pytest.raises(ms.MambaError):
             ms.bwd_workspace_bytes(bad, ms.DIR_FWD)
 
@@ -175,8 +179,8 @@ def test_bwd_workspace_and_validation(lib):
     assert bwd(d, dB=None) == E.MAMBA_ERR_INVALID
     assert bwd(dims(batch=0)) == E.MAMBA_ERR_INVALID
     assert bwd(d, mode=7) == E.MAMBA_ERR_INVALID
-    assert bwd(dims(dstate=64)) == E.MAMBA_ERR_UNSUPPORTED
-    assert bwd(dims(dstate=40)) == E.MAMBA_ERR_UNSUPPORTED
+    assert bwd(dims(dstate=65)) == E.MAMBA_ERR_UNSUPPORTED
+    assert bwd(dims(dstate=40)) == E.MAMBA_ERR_WORKSPACE  # built (state groups); no workspace given
     assert bwd(dims(dim=36, dtype=ms.DTYPE_F32)) == E.MAMBA_ERR_UNSUPPORTED  # forward-only channel count
     assert bwd(d, dz=FAKE + 2) == E.MAMBA_ERR_UNSUPPORTED
     assert bwd(d) == E.MAMBA_ERR_WORKSPACE  # the backward pass always needs its workspace
@@ -199,9 +203,10 @@ def test_saved_state_size_and_fwd_save_validation(lib):
     assert ms.saved_bytes(d, ms.DIR_FWD, True) == ck + Bz * L * Dm * 4
     cross = dims(seqlen=96, height=8, width=12)
     assert ms.saved_bytes(cross, ms.DIR_CROSS2D, True) == 4 * Bz * 6 * Dm * N * 4 + 4 * Bz * 96 * Dm * 4
-    # above 16 states, every 32nd position
+    # 17..32 states, every 32nd position; above 32 (state groups of 16), every 16th again
     assert ms.saved_bytes(dims(dstate=32), ms.DIR_FWD, False) == (Bz * 4 * Dm * 32 * 4 + 255) // 256 * 256
-    for bad in (dims(dstate=64), dims(dstate=33), dims(seqlen=0), dims(dim=60)):
+    assert ms.saved_bytes(dims(dstate=48), ms.DIR_FWD, False) == (Bz * 7 * Dm * 48 * 4 + 255) // 256 * 256
+    for bad in (dims(dstate=65), dims(seqlen=0), dims(dim=60)):
         with pytest.raises(ms.MambaError):
             ms.saved_bytes(bad, ms.DIR_FWD, False)
 
@@ -216,8 +221,8 @@ def test_saved_state_size_and_fwd_save_validation(lib):
     assert fwd_save(d, saved=None) == E.MAMBA_ERR_INVALID
     assert fwd_save(d, out=None) == E.MAMBA_ERR_INVALID
     assert fwd_save(dims(batch=0)) == E.MAMBA_ERR_INVALID
-    assert fwd_save(dims(dstate=64)) == E.MAMBA_ERR_UNSUPPORTED  # what the backward pass cannot read
-    assert fwd_save(dims(dstate=48)) == E.MAMBA_ERR_UNSUPPORTED
+    assert fwd_save(dims(dstate=65)) == E.MAMBA_ERR_UNSUPPORTED  # what the backward pass cannot read
+    assert fwd_save(dims(dstate=48)) == E.MAMBA_ERR_WORKSPACE  # built; ck is too small for 48 states
     assert fwd_save(d, saved=FAKE + 4) == E.MAMBA_ERR_UNSUPPORTED
     assert fwd_save(d, saved_bytes=ck - 1) == E.MAMBA_ERR_WORKSPACE
     assert fwd_save(d, z=FAKE) == E.MAMBA_ERR_WORKSPACE  # with a gate the rows are saved too

@@ -3,7 +3,8 @@ the fp64 backward oracle on the same seeded inputs.
 
 The training pass recomputes the states and runs the adjoint recurrence
 [MFS §5; S4M §2.3].  Small cases span several 16-channel blocks and 32-step
-segments with ragged tails, every direction mode, state sizes 1..16, both
+segments with ragged tails, every direction mode, state sizes 1..64 (above 32 in
+groups of 16 states, the last one partial at 33 and 40), both
 input-term rules, softplus on and off, the optional gate, skip, bias and
 initial state, and the time-split forward recompute.  The specified workloads
 run at full size, checked on a channel subset over the whole batch (every
@@ -110,6 +111,13 @@ SMALL = [
     ("n24_cross2d_f32_exact", W("n24_cross", 1, 16, 42, 24, I.DIR_CROSS2D, "f32", True, 62, 6, 7), True, True,
      False, True),
     ("n20_split_bwd_bf16", W("n20_split", 1, 16, 2200, 20, I.DIR_BWD, "bf16", True, 63), True, False, True, True),
+    # above 32 states: groups of 16 states (the last group partial at 33 and 40)
+    ("n64_fwd_bf16_init", W("n64_fwd", 2, 40, 90, 64, I.DIR_FWD, "bf16", True, 64), True, False, True, True),
+    ("n48_bidir_f32_exact", W("n48_bidir", 1, 24, 70, 48, I.DIR_BIDIR, "f32", True, 65), True, True, False, True),
+    ("n40_cross2d_bf16_init", W("n40_cross", 1, 16, 48, 40, I.DIR_CROSS2D, "bf16", True, 66, 6, 8), True, False,
+     True, True),
+    ("n33_fwd_f32_nosoftplus", W("n33_fwd", 2, 24, 41, 33, I.DIR_FWD, "f32", True, 67), False, False, False, True),
+    ("n64_split_bwd_f32", W("n64_split", 1, 16, 2300, 64, I.DIR_BWD, "f32", True, 68), True, False, True, True),
 ]
 
 
@@ -220,7 +228,8 @@ def saved_vs_recompute(name, w, xd, dout, init=None, softplus=True, exact=False)
 SAVED = [c for c in SMALL if c[0] in ("fwd_bf16", "fwd_f32_n4_exact_init", "bwd_bf16_n8", "bidir_f32_init",
                                       "cross2d_bf16", "cross2d_f32_n1_gated", "split_fwd_bf16", "split_bidir_f32",
                                       "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16", "n32_fwd_bf16_init",
-                                      "n3_fwd_f32_init", "n12_bidir_bf16")]
+                                      "n3_fwd_f32_init", "n12_bidir_bf16", "n64_fwd_bf16_init",
+                                      "n40_cross2d_bf16_init", "n64_split_bwd_f32")]
 
 
 @pytest.mark.parametrize("case", SAVED, ids=[c[0] for c in SAVED])
