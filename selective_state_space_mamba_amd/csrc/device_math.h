@@ -250,6 +250,35 @@ __device__ __forceinline__ void buf_store(uint16_t v, __amdgpu_buffer_rsrc_t r, 
 __device__ __forceinline__ void buf_store(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)voff, (int)soff, 0);
 }
+// Two adjacent channels of one token row: one 32-bit (bf16) or 64-bit (f32)
+// buffer load, and the matching store of two results.
+template <typename T>
+struct Pair;
+template <>
+struct Pair<uint16_t> {
+  uint32_t w;
+  __device__ __forceinline__ void zero() { w = 0; }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    w = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ float get(int j) const { return __uint_as_float(j ? (w & 0xffff0000u) : (w << 16)); }
+};
+template <>
+struct Pair<float> {
+  u32x2 w;
+  __device__ __forceinline__ void zero() { w = u32x2{0u, 0u}; }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
+  }
+  __device__ __forceinline__ float get(int j) const { return __uint_as_float(w[j]); }
+};
+__device__ __forceinline__ void store_pair(float y0, float y1, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(y0, y1), r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ void store_pair(float y0, float y1, __amdgpu_buffer_rsrc_t r, uint32_t voff, float*) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(y0), __float_as_uint(y1)}, r, (int)voff, 0, 0);
+}
+
 __device__ __forceinline__ uint16_t to_bf16(float y) { return (uint16_t)(pack_bf16x2(y, 0.0f) & 0xffffu); }
 __device__ __forceinline__ void store_out(float y, __amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint16_t*) {
   buf_store(to_bf16(y), r, voff, soff);

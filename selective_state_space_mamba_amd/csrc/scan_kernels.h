@@ -162,7 +162,21 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // Vim-224 from 245 to 238 µs when it still ran on them.
   constexpr int P_EPI = 0;
   constexpr int P_STAGE = CB == 16 ? 0 : 2;
-  __shared__ float s_y[AGG ? 1 : NY][AGG ? 1 : CB][AGG ? 4 : YS];
+  // Staging and epilogue ownership.  With 16-channel blocks (PAIR) a thread
+  // stages and stores two adjacent channels at PPT consecutive positions of a
+  // tile: one 32-bit (bf16) or 64-bit (f32) load per tensor and position and
+  // one store per position, half the memory instructions of one channel at
+  // two positions.  With 64-channel blocks a thread keeps one channel at TPT
+  // positions (the wave's row offsets are then scalars).
+  constexpr bool PAIR = CB == 16;
+  constexpr int NPR = CB / 2;                           // channel pairs per block
+  constexpr int PPT = PAIR ? TT * NPR / NT : TPT;       // positions staged per thread
+  constexpr int EPT = PAIR ? 2 * PPT : TPT;             // (position, channel) elements per thread
+  static_assert(!PAIR || (TT * NPR) % NT == 0, "a tile's pairs split evenly over the threads");
+  // partial readouts: [group][position][channel] with 16-channel blocks (two
+  // adjacent channels of a position are one 8-byte read), [group][channel][position]
+  // with 64 (each thread writes 4 steps of its channel at once)
+  __shared__ float s_y[AGG ? 1 : NY][AGG ? 1 : (PAIR ? TT : CB)][AGG ? 4 : (PAIR ? CB : YS)];
 
   const int tid = threadIdx.x;
   const int cl = tid % CB;  // channel within the block
@@ -251,8 +265,19 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       }
     }
   }
-  const float bias = (dvalid && p.delta_bias) ? p.delta_bias[k * D + d] : 0.f;
-  const float Dd = (dvalid && p.D) ? p.D[k * D + d] : 0.f;
+  // the staging and epilogue elements of this thread: channels e0 (and e0 + 1
+  // with PAIR) at positions ppos0 .. ppos0 + PPT - 1 of each tile; pairs are
+  // aligned and D is a multiple of 8, so both channels of a pair exist or neither
+  const int e0 = PAIR ? 2 * (tid % NPR) : cl;
+  const int ppos0 = PAIR ? (tid / NPR) * PPT : ng * TPT;
+  const bool evalid = d0 + e0 < D;
+  float bias2[2], Dd2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int de = d0 + e0 + (PAIR ? j : 0);
+    bias2[j] = (evalid && p.delta_bias) ? p.delta_bias[k * D + de] : 0.f;
+    Dd2[j] = (evalid && p.D) ? p.D[k * D + de] : 0.f;
+  }
   // The state registers may still be waiting on the loads above; settle them
   // here so that no wait on global loads lands inside the scan loop, where it
   // would also wait for the next tile's prefetch.
@@ -268,14 +293,24 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // raw (undecoded) loads of one tile; two sets rotate so that a tile's loads
   // are issued two tiles before it is staged
   struct Raw {
-    TIn dl[TPT], u[TPT], z[TPT];
+    Pair<TIn> pdl[PAIR ? PPT : 1], pu[PAIR ? PPT : 1], pz[PAIR ? PPT : 1];
+    TIn dl[PAIR ? 1 : TPT], u[PAIR ? 1 : TPT], z[PAIR ? 1 : TPT];
     Small<TIn, EQ> B[BCI], C[BCI];
   };
   Raw r0, r1;
-  float Du[TPT], gate[TPT], folded[TPT];
+  float Du[EPT], gate[EPT], folded[EPT];
+  if constexpr (PAIR) {
 #pragma unroll
-  for (int i = 0; i < TPT; ++i) {
-    r0.dl[i] = r0.u[i] = r0.z[i] = r1.dl[i] = r1.u[i] = r1.z[i] = TIn(0);
+    for (int i = 0; i < PPT; ++i) {
+      r0.pdl[i].zero(); r0.pu[i].zero(); r0.pz[i].zero();
+      r1.pdl[i].zero(); r1.pu[i].zero(); r1.pz[i].zero();
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) r0.dl[i] = r0.u[i] = r0.z[i] = r1.dl[i] = r1.u[i] = r1.z[i] = TIn(0);
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
     Du[i] = 0.f;
     gate[i] = 1.f;
     folded[i] = 0.f;
@@ -291,10 +326,11 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // Element offsets of this thread's channel; rows outside the chunk and
   // channels beyond D are clamped to valid addresses (their values are zeroed
   // at staging and never stored).
-  const int dlast = D - 1 - d0;
-  const uint32_t voff_in = (uint32_t)(d0 + min(cl, dlast)) * ES;
-  const uint32_t voff_ws = (uint32_t)(d0 + min(cl, dlast)) * 4u;
-  const uint32_t voff_out = (uint32_t)(d0 + min(cl, dlast)) * ES;
+  // (a pair's first channel is clamped to D - 2: D is even)
+  const int dlast = D - (PAIR ? 2 : 1) - d0;
+  const uint32_t voff_in = (uint32_t)(d0 + min(e0, dlast)) * ES;
+  const uint32_t voff_ws = (uint32_t)(d0 + min(e0, dlast)) * 4u;
+  const uint32_t voff_out = (uint32_t)(d0 + min(e0, dlast)) * ES;
   const bool dfull = d0 + CB <= D;
   // Byte offset of the token row of scan position pp (clamped into the chunk)
   // for a row of D elements of es bytes.  Tokens and row strides are below
@@ -303,15 +339,25 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
   // Loads are issued unconditionally (rows clamped into the chunk), so the
   // wait before staging covers exactly the older of the two tiles in flight.
   auto load_tile = [&](int p0, Raw& r) {
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      // the row offset is a scalar only when the wave's rows are one row (CB = 64)
-      const uint32_t roff = row_off(p0 + ng * TPT + i, ES);
-      const uint32_t soff = CB == 64 ? roff : 0u;
-      const uint32_t voff = CB == 64 ? voff_in : voff_in + roff;
-      r.dl[i] = buf_load(rs_dl, voff, soff, (TIn*)nullptr);
-      r.u[i] = buf_load(rs_u, voff, soff, (TIn*)nullptr);
-      if (gated) r.z[i] = buf_load(rs_z, voff, soff, (TIn*)nullptr);
+      for (int i = 0; i < PPT; ++i) {
+        const uint32_t voff = voff_in + row_off(p0 + ppos0 + i, ES);
+        r.pdl[i].load(rs_dl, voff);
+        r.pu[i].load(rs_u, voff);
+        if (gated) r.pz[i].load(rs_z, voff);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        // the row offset is a scalar only when the wave's rows are one row (CB = 64)
+        const uint32_t roff = row_off(p0 + ng * TPT + i, ES);
+        const uint32_t soff = CB == 64 ? roff : 0u;
+        const uint32_t voff = CB == 64 ? voff_in : voff_in + roff;
+        r.dl[i] = buf_load(rs_dl, voff, soff, (TIn*)nullptr);
+        r.u[i] = buf_load(rs_u, voff, soff, (TIn*)nullptr);
+        if (gated) r.z[i] = buf_load(rs_z, voff, soff, (TIn*)nullptr);
+      }
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
@@ -325,6 +371,52 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
 
   auto stage_tile = [&](int p0, const Raw& r) {
     __builtin_amdgcn_s_setprio(P_STAGE);
+    if constexpr (PAIR) {
+      // (Δ', Δu) of channels e0, e0 + 1 at positions ppos0 .. ppos0 + PPT - 1
+      float dd[2][2 * PPT];
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int tt = ppos0 + i;
+        const float okf = ((p0 + tt < pend) && evalid) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float x = r.pdl[i].get(j) + bias2[j];
+          const float dl = (p.softplus ? softplus_log2(x) : x * kLog2e) * okf;  // Δ' = Δ·log2 e
+          const float uu = r.pu[i].get(j) * okf;
+          dd[j][2 * i] = dl;
+          dd[j][2 * i + 1] = EXACT ? uu : dl * uu;
+          if constexpr (!AGG) {
+            Du[2 * i + j] = Dd2[j] * uu;
+            if (gated) gate[2 * i + j] = silu_f(r.pz[i].get(j));
+          }
+        }
+      }
+      if constexpr (!AGG) {
+        if (fold) {
+          // the folded row at this thread's epilogue elements, read a whole
+          // tile before its use
+#pragma unroll
+          for (int i = 0; i < PPT; ++i) {
+            Pair<float> f2;
+            f2.load(rs_fold, voff_ws + row_off(p0 + ppos0 + i, 4u));
+            folded[2 * i] = f2.get(0);
+            folded[2 * i + 1] = f2.get(1);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float* row = &s_dd[(e0 + j) * DS + 2 * ppos0];
+        if constexpr (PPT == 1) {
+          *reinterpret_cast<float2*>(row) = make_float2(dd[j][0], dd[j][1]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < PPT / 2; ++m)
+            *reinterpret_cast<float4*>(row + 4 * m) =
+                make_float4(dd[j][4 * m], dd[j][4 * m + 1], dd[j][4 * m + 2], dd[j][4 * m + 3]);
+        }
+      }
+    } else {
     float dd[2 * TPT];
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -333,13 +425,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
       // clamped rows and channels), then zero rows past the chunk end and
       // channels past D by a 0/1 factor -- cheaper than a select per value.
       const float okf = ((p0 + tt < pend) && dvalid) ? 1.f : 0.f;
-      const float x = to_f32(r.dl[i]) + bias;
+      const float x = to_f32(r.dl[i]) + bias2[0];
       const float dl = (p.softplus ? softplus_log2(x) : x * kLog2e) * okf;  // Δ' = Δ·log2 e
       const float uu = to_f32(r.u[i]) * okf;
       dd[2 * i] = dl;
       dd[2 * i + 1] = EXACT ? uu : dl * uu;
       if constexpr (!AGG) {
-        Du[i] = Dd * uu;
+        Du[i] = Dd2[0] * uu;
         if (gated) gate[i] = silu_f(to_f32(r.z[i]));
       }
     }
@@ -359,6 +451,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     for (int m = 0; m < TPT / 2; ++m)
       *reinterpret_cast<float4*>(&s_dd[cl * DS + 2 * ng * TPT + 4 * m]) =
           make_float4(dd[4 * m], dd[4 * m + 1], dd[4 * m + 2], dd[4 * m + 3]);
+    }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
       const int q = tid + i * NT;
@@ -455,7 +548,7 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         const float z02 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
         const float z13 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
         const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(z02), __float_as_uint(z13), false, false);
-        s_y[ng >> 2][cl][tt + (ng & 3)] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+        s_y[ng >> 2][tt + (ng & 3)][cl] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
       } else {
         *reinterpret_cast<float4*>(&s_y[ng][cl][tt]) = make_float4(y[0], y[1], y[2], y[3]);
       }
@@ -494,7 +587,34 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
     }
     __builtin_amdgcn_s_setprio(P_EPI);
     __syncthreads();
-    if constexpr (!AGG) {
+    if constexpr (!AGG && PAIR) {
+      // epilogue: channels e0, e0 + 1 at positions ppos0 .. ppos0 + PPT - 1
+      // (the partials added in group order, as below)
+#pragma unroll
+      for (int i = 0; i < PPT; ++i) {
+        const int tt = ppos0 + i;
+        float y0 = Du[2 * i], y1 = Du[2 * i + 1];
+#pragma unroll
+        for (int g = 0; g < NY; ++g) {
+          const float2 v = *reinterpret_cast<const float2*>(&s_y[g][tt][e0]);
+          y0 += v.x;
+          y1 += v.y;
+        }
+        const int pp = p0 + tt;
+        if (pp < pend && evalid) {
+          if (p.ws_y && !fold) store_pair(y0, y1, rs_ws, voff_ws + row_off(pp, 4u), (float*)nullptr);
+          if (direct) {
+            float o0 = fold ? folded[2 * i] + y0 : y0;
+            float o1 = fold ? folded[2 * i + 1] + y1 : y1;
+            if (gated) {
+              o0 *= gate[2 * i];
+              o1 *= gate[2 * i + 1];
+            }
+            store_pair(o0, o1, rs_out, voff_out + row_off(pp, ES), (TIn*)nullptr);
+          }
+        }
+      }
+    } else if constexpr (!AGG) {
       // epilogue: this thread's channel at positions ng*TPT .. ng*TPT+TPT-1
       float yv[TPT];
 #pragma unroll
