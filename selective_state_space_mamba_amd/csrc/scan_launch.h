@@ -53,7 +53,10 @@ inline constexpr int threads_of(int N, int g16 = 1) { return layout_of(N, g16).c
 // N = 16 win once 1 state per thread would give 24 or more waves per SIMD
 // (batch 64: 942 -> 910 µs; Vim-224: 220 -> 210 µs) and lose below 12
 // (batch 32: 482 -> 497; the 130M layer at 3 waves per SIMD: 140 -> 180).
-inline constexpr int64_t kG2Waves = 16 * 1024;
+#ifndef MSCAN_G2_WAVES
+#define MSCAN_G2_WAVES (16 * 1024)
+#endif
+inline constexpr int64_t kG2Waves = MSCAN_G2_WAVES;
 
 // Workspace of a forward pass, in this order (each region 256-byte aligned):
 // the per-direction fp32 rows, the time-split aggregates (end states, ΣΔ'),
