@@ -39,6 +39,14 @@ namespace mscan {
 #ifndef MSCAN_BWD_WAVES
 #define MSCAN_BWD_WAVES 2  // waves per SIMD the adjoint kernel's register budget is sized for (3 spills)
 #endif
+#ifndef MSCAN_BWD_WAVES16
+// The same for 16 thread rows (N = 9..16 and the state groups above 32): 128
+// VGPRs with 1 to 3 spilled, 4 waves per SIMD.  Measured on MI355X against the
+// 2-wave budget (129 VGPRs, 3 waves), both builds in one process: Vim-224's
+// backward 878 -> 818 us; the 130M layer, whose rows fill 3 waves per SIMD,
+// and the cross scan unchanged (545 / 548, 2225 / 2226).
+#define MSCAN_BWD_WAVES16 4
+#endif
 #ifndef MSCAN_BWD_WAVES_EXACT
 #define MSCAN_BWD_WAVES_EXACT 1  // the same for the exact rule (with 16-position segments it fits 198 VGPRs anyway)
 #endif
@@ -251,7 +259,8 @@ __device__ __forceinline__ float row_sum_transpose16(const float (&v)[16], uint3
 // GRP: a state group of a larger N (p.ngroups groups of NP states; the row
 // stride of A, B, C, the checkpoints and the per-state gradients is p.N).
 template <typename TIn, int NP, bool FULL, bool EXACT, bool AGG, bool GRP = false>
-__global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP), EXACT ? MSCAN_BWD_WAVES_EXACT : MSCAN_BWD_WAVES)
+__global__ void __launch_bounds__(16 * (NP < 4 ? 4 : NP),
+                                  EXACT ? MSCAN_BWD_WAVES_EXACT : (NP == 16 ? MSCAN_BWD_WAVES16 : MSCAN_BWD_WAVES))
     scan_bwd_kernel(const BwdParams p) {
   constexpr int CB = 16;
   constexpr int NGP = NP < 4 ? 4 : NP;  // thread rows
