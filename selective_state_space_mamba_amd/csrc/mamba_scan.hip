@@ -46,7 +46,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 #define MSCAN_FORCE_KERNEL 0  // 1: the channel-block kernel wherever it applies, 2: the row kernel everywhere
 #endif
 #ifndef MSCAN_ROW_TARGET_WAVES
-#define MSCAN_ROW_TARGET_WAVES 4096  // resident waves wanted from the row kernel's split (up to 16 states)
+#define MSCAN_ROW_TARGET_WAVES 8192  // waves wanted from the row kernel's split (up to 16 states)
 #endif
 #ifndef MSCAN_ROW_MIN_CHUNK
 #define MSCAN_ROW_MIN_CHUNK 256  // shortest time chunk of the row kernel's split
@@ -81,10 +81,11 @@ int plan_rows(const mamba_dims* g, int K, Plan* pl) {
   pl->prio = 0;
   pl->nblk_d = (int)((g->dim + 63) / 64);
   const int64_t rows = (int64_t)K * g->batch * pl->nblk_d;
-  // Up to 16 states the kernel fits 4 waves per SIMD (at most 119 VGPRs), so
-  // the split aims at one round of 4 per SIMD; measured on MI355X with both
-  // builds in one process, the 262k-token context in 128 chunks instead of 96
-  // (3 per SIMD): 3997 -> 3687 µs.  Larger states keep 3 per SIMD.
+  // Up to 16 states the kernel fits 4 waves per SIMD (at most 119 VGPRs), and
+  // the split aims at two rounds of 4 per SIMD.  Measured on MI355X with the
+  // builds loaded side by side in one process, the 262k-token context in 96
+  // chunks (3 waves per SIMD) 3997 µs, 128 (one round of 4) 3687-3709, 256
+  // (two rounds) 3277-3307, 512 3774.  Larger states keep 3 per SIMD.
   const int64_t target = pl->np <= 16 ? MSCAN_ROW_TARGET_WAVES : MSCAN_TARGET_WAVES;
   int64_t nch = 1;
   if (rows < target) {
