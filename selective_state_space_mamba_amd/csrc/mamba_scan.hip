@@ -213,6 +213,9 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
 // time-split carries.
 constexpr int kBwdBlock = 16;     // channels per workgroup of scan_bwd_kernel
 constexpr int kBwdSlots = 512;    // adjoint workgroups resident at once (2 per CU; 1 at N = 32)
+#ifndef MSCAN_BWD_SLOTS16
+#define MSCAN_BWD_SLOTS16 1024  // the same with 16 thread rows (4 waves per SIMD: 4 per CU)
+#endif
 constexpr int kBwdMinChunk = 1024;  // shortest time chunk of a split adjoint
 constexpr int kBwdGroup = 16;     // states per group above 32 states
 struct BwdPlan {
@@ -248,9 +251,16 @@ int make_bwd_plan(const mamba_dims* g, int mode, BwdPlan* bp) {
   // Time split of the adjoint when its rows fill less than one round of
   // workgroups: up to two rounds, chunks of at least kBwdMinChunk positions.
   const int64_t rows = (int64_t)bp->nblk * Bz * K * G;
-  const int64_t slots = (N > 16 && G == 1) ? kBwdSlots / 2 : kBwdSlots;
+  // Split below half a round of 16-thread-row workgroups (4 per CU since the
+  // adjoint's 4-wave budget), into chunks for two rounds.  Measured on MI355X
+  // with the builds side by side in one process: two rounds of 1024 instead
+  // of 512 slots, the 97k-token Vim's backward 5239 -> 4479 µs, the 262k-token
+  // context's 17271 -> 16824; splitting the 130M layer's 768 rows (2 chunks)
+  // 544 -> 623, so it stays unsplit.
+  const int64_t slots = (N > 16 && G == 1) ? kBwdSlots / 2 : (N > 8 ? MSCAN_BWD_SLOTS16 : kBwdSlots);
+  const int64_t split_below = (N > 16 && G == 1) ? kBwdSlots / 2 : kBwdSlots;
   int64_t nch = 1;
-  if (rows < slots) {
+  if (rows < split_below) {
     nch = (2 * slots + rows - 1) / rows;
     if (nch > L / kBwdMinChunk) nch = L / kBwdMinChunk;
     if (nch > 256) nch = 256;
