@@ -76,6 +76,7 @@ bool choose_rows(const mamba_dims* g, int K) {
 int plan_rows(const mamba_dims* g, int K, Plan* pl) {
   const int64_t L = g->seqlen, N = g->dstate;
   pl->row = 1;
+  pl->tile = kTile;  // (unused by the row kernel)
   pl->cb = 64;
   pl->g = (int)N;
   pl->prio = 0;
@@ -190,8 +191,15 @@ int make_plan(const mamba_dims* g, int mode, Plan* pl) {
   // batch-32 130M-shaped layer at 12: 478 µs with it, 482 without)
   pl->prio = waves * nch < 16 * 1024 ? 1 : 0;
   pl->nblk_d = (int)((g->dim + cb - 1) / cb);
+  // 64-position tiles for one state per thread at N = 16 on sequences of
+  // 1024 positions or more: half the barriers and per-tile work per position.
+  // Measured on MI355X with the builds side by side in one process (µs): the
+  // cross scan 595.5 -> 564.8, the 130M layer 133.9 -> 132.0; two states per
+  // thread lose with them (Vim-224 189 -> 263, the 97k-token Vim 1157 ->
+  // 1289), and short sequences would pad a larger share of their last tile.
+  pl->tile = (N == 16 && g16 == 1 && L >= 1024) ? 2 * kTile : kTile;
   int64_t clen = (L + nch - 1) / nch;
-  clen = (clen + kTile - 1) / kTile * kTile;
+  clen = (clen + pl->tile - 1) / pl->tile * pl->tile;
   nch = (L + clen - 1) / clen;
   if (pl->nblk_d * nch * g->batch * K > INT32_MAX) return MAMBA_ERR_UNSUPPORTED;
   pl->nchunks = (int)nch;

@@ -18,10 +18,12 @@
 //     records its end state S_c and ΣΔ over the chunk (the chunk's decay is
 //     exp(A·ΣΔ) since Ā_t = exp(Δ_t·A)); the output pass folds the aggregates
 //     of the chunks before it into its starting state;
-//   * the chunk is streamed in tiles of TT scan positions: u, Δraw, z are
-//     read one element per thread per token through buffer descriptors (each
-//     token's channel row is contiguous in the token-major layout whatever the
-//     traversal order), two tiles ahead of use, then staged in LDS as
+//   * the chunk is streamed in tiles of TT scan positions (32, or 64 for one
+//     state per thread at N = 16 on long sequences): u, Δraw, z are read
+//     through buffer descriptors, two adjacent channels per thread and load
+//     with 16-channel blocks (each token's channel row is contiguous in the
+//     token-major layout whatever the traversal order), two tiles ahead of
+//     use, then staged in LDS as
 //     (Δ', Δ'·u) pairs -- Δ' = Δ·log2 e, softplus and the product computed once
 //     per (token, channel) -- next to B·ln 2 and C rows shared by the channels;
 //   * per scan step and state: Ā = 2^(Δ'·A) = exp(Δ·A) (one v_exp_f32),
@@ -124,7 +126,9 @@ __device__ __forceinline__ int logical_block(int bid, int nblocks, int S) {
 // staging and the epilogue the same thread owns channel c and the TPT = TT/NG
 // consecutive scan positions ng*TPT .. ng*TPT+TPT-1 of each tile.
 template <typename TIn, int N, int G, int CB, int TT, bool AGG, bool EXACT>
-__global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams p) {
+// (64-position tiles: a 4-waves-per-SIMD register budget, 128 VGPRs; without
+// it the in-tile checkpoints take the kernel to 132 and 3 waves)
+__global__ void __launch_bounds__(CB * N / G, TT == 64 ? 4 : 1) scan_chunk_kernel(const ScanParams p) {
   constexpr int NG = N / G;    // state groups per channel
   constexpr int NT = CB * NG;  // threads per workgroup
   static_assert(NT % 64 == 0 && NT <= 1024, "whole waves");
@@ -566,7 +570,13 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
         if (4 * q < tend) {
           if (q + PDQ < NQ) read_ops(ring[(q + PDQ) % (PDQ + 1)], 4 * (q + PDQ));
           quad(ring[q % (PDQ + 1)], 4 * q);
-          if (4 * q + 4 == 16 && TT > 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
+          // (inside the tile, the state before every ckpt_every-th position:
+          // ckpt_every is 16 or 32)
+          if constexpr (TT == 32) {
+            if (4 * q + 4 == 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
+          } else if (4 * q + 4 < TT && (4 * q + 4) % 16 == 0 && ((4 * q + 4) % 32 == 0 || p.ckpt_every == 16)) {
+            checkpoint(p0 + 4 * q + 4);
+          }
         }
       }
     } else {
@@ -580,7 +590,11 @@ __global__ void __launch_bounds__(CB * N / G) scan_chunk_kernel(const ScanParams
           if (tt + 4 < tend) {
             read_ops(o0, min(tt + 8, TT - 4));  // the last prefetch re-reads rows that go unused
             quad(o1, tt + 4);
-            if (tt + 8 == 16 && TT > 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
+            if constexpr (TT == 32) {
+              if (tt + 8 == 16 && p.ckpt_every == 16) checkpoint(p0 + 16);
+            } else if (tt + 8 < TT && (tt + 8) % 16 == 0 && ((tt + 8) % 32 == 0 || p.ckpt_every == 16)) {
+              checkpoint(p0 + tt + 8);
+            }
           }
         }
       }

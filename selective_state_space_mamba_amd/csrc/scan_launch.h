@@ -63,6 +63,7 @@ inline constexpr int64_t kG2Waves = MSCAN_G2_WAVES;
 // and for the row kernel the fp32 copies of B and C.
 struct Plan {
   int K, Ku, cb, g, nblk_d, nchunks, chunk_len, prio;
+  int tile;  // scan positions per LDS tile of the channel-block kernel (kTile or 2 kTile)
   int row;  // 1: scan_row_kernel (one channel per lane, all states in registers); 0: scan_chunk_kernel
   int np;   // the row kernel's power-of-two state count (>= N)
   size_t ws_y_bytes, agg_state_bytes, agg_dsum_bytes, bc_bytes;
@@ -111,15 +112,15 @@ int launch_merge(const ScanParams& p, hipStream_t stream) {
 // alone fills a quarter of the GPU and loses: 999 vs 674.
 inline bool folds(const ScanParams& p) { return MSCAN_FOLD && p.fold && p.K == 2 && p.out && p.ws_y; }
 
-template <typename TIn, int N, int G16, bool EXACT>
-int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
+template <typename TIn, int N, int G16, bool EXACT, int TT>
+int launch_chunks_tt(ScanParams p, const Plan& pl, hipStream_t stream) {
   constexpr Layout lay = layout_of(N, G16);
   constexpr int NT = threads_of(N, G16);
   if (pl.nchunks > 1) {
     p.grid_chunks = pl.nchunks - 1;
     p.prio = pl.prio;
     const unsigned blocks = (unsigned)(pl.nblk_d * p.grid_chunks * p.Bsz * p.K);
-    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, true, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, TT, true, EXACT>), dim3(blocks), dim3(NT), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return MAMBA_ERR_HIP;
   }
   p.grid_chunks = pl.nchunks;
@@ -130,7 +131,7 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
     q.kbase = kbase;
     q.fold = fold;
     const unsigned blocks = (unsigned)(pl.nblk_d * q.grid_chunks * q.Bsz * kcount);
-    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, kTile, false, EXACT>), dim3(blocks), dim3(NT), 0,
+    hipLaunchKernelGGL((scan_chunk_kernel<TIn, N, lay.g, lay.cb, TT, false, EXACT>), dim3(blocks), dim3(NT), 0,
                        stream, q);
     return hipGetLastError() == hipSuccess ? MAMBA_OK : MAMBA_ERR_HIP;
   };
@@ -141,6 +142,16 @@ int launch_chunks(ScanParams p, const Plan& pl, hipStream_t stream) {
     return rc != MAMBA_OK ? rc : run(p.K - 1, 1, 1);
   }
   return run(0, p.K, 0);
+}
+
+// 64-position tiles for one state per thread at N = 16 on long sequences
+// (Plan::tile, set by the plan), 32 elsewhere.
+template <typename TIn, int N, int G16, bool EXACT>
+int launch_chunks(const ScanParams& p, const Plan& pl, hipStream_t stream) {
+  if constexpr (N == 16 && G16 == 1) {
+    if (pl.tile == 2 * kTile) return launch_chunks_tt<TIn, N, G16, EXACT, 2 * kTile>(p, pl, stream);
+  }
+  return launch_chunks_tt<TIn, N, G16, EXACT, kTile>(p, pl, stream);
 }
 
 template <typename TIn, int N, bool EXACT>

@@ -118,6 +118,10 @@ SMALL = [
      True, True),
     ("n33_fwd_f32_nosoftplus", W("n33_fwd", 2, 24, 41, 33, I.DIR_FWD, "f32", True, 67), False, False, False, True),
     ("n64_split_bwd_f32", W("n64_split", 1, 16, 2300, 64, I.DIR_BWD, "f32", True, 68), True, False, True, True),
+    # the forward recompute in 64-position tiles (checkpoints inside the tile)
+    ("t64_fwd_bf16_init", W("t64_fwd", 2, 40, 1100, 16, I.DIR_FWD, "bf16", True, 69), True, False, True, True),
+    ("t64_cross2d_f32", W("t64_cross", 1, 16, 1024, 16, I.DIR_CROSS2D, "f32", True, 70, 32, 32), True, False, False,
+     True),
 ]
 
 
@@ -229,7 +233,8 @@ SAVED = [c for c in SMALL if c[0] in ("fwd_bf16", "fwd_f32_n4_exact_init", "bwd_
                                       "cross2d_bf16", "cross2d_f32_n1_gated", "split_fwd_bf16", "split_bidir_f32",
                                       "L1_D8_bf16_n2", "exact_nosoftplus_init_bf16", "n32_fwd_bf16_init",
                                       "n3_fwd_f32_init", "n12_bidir_bf16", "n64_fwd_bf16_init",
-                                      "n40_cross2d_bf16_init", "n64_split_bwd_f32")]
+                                      "n40_cross2d_bf16_init", "n64_split_bwd_f32", "t64_fwd_bf16_init",
+                                      "t64_cross2d_f32")]
 
 
 @pytest.mark.parametrize("case", SAVED, ids=[c[0] for c in SAVED])

@@ -90,6 +90,11 @@ SMALL = {
     "split_long_bidir_f32": I.Workload("split_long_bidir_f32", 1, 64, 8500, 16, I.DIR_BIDIR, "f32", True, 29),
     "split_long_fwd_bf16_n8": I.Workload("split_long_fwd_bf16_n8", 1, 64, 9000, 8, I.DIR_FWD, "bf16", True, 30),
     "split_long_bidir_f32_n4": I.Workload("split_long_bidir_f32_n4", 1, 72, 5000, 4, I.DIR_BIDIR, "f32", True, 31),
+    # one state per thread at N = 16 on 1024 positions or more: 64-position tiles
+    # (ragged last tile, the bidirectional fold, the cross scan's column order)
+    "t64_fwd_f32": I.Workload("t64_fwd_f32", 2, 48, 1100, 16, I.DIR_FWD, "f32", True, 34),
+    "t64_bidir_bf16": I.Workload("t64_bidir_bf16", 2, 40, 1500, 16, I.DIR_BIDIR, "bf16", True, 35),
+    "t64_cross2d_bf16": I.Workload("t64_cross2d_bf16", 1, 32, 1024, 16, I.DIR_CROSS2D, "bf16", False, 36, 32, 32),
 }
 
 
